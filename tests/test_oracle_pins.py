@@ -1,0 +1,276 @@
+"""Pins of the CPU oracle against things other than itself: exact rational
+brute force, integer arithmetic, closed forms, invariants, library routines
+and the pages' non-associativity example.  CPU only."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_reduction_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_fraction(bits):
+    """Exact value of one bf16 bit pattern from its fields (sign, 8-bit
+    exponent, 7-bit fraction), independent of any float conversion."""
+    bits = int(bits)
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    assert e != 0xFF, "finite inputs only"
+    if e == 0:
+        return sign * Fraction(f, 1 << 7) * Fraction(1, 1 << 126)
+    val = Fraction(128 + f, 128)
+    return sign * (val * (Fraction(2) ** (e - 127)))
+
+
+def rand_bf16(shape, rng, scale=1.0):
+    f = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return inputs.f32_bits_to_bf16_bits(f)
+
+
+# --- bf16 decoding and the cast step --------------------------------------
+
+def test_bf16_decode_known_values():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x0001, 0x7F7F, 0x4049],
+                    np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127,
+            3.140625]
+    got = oracle.bf16_to_f64(bits)
+    for g, w, b in zip(got, want, bits):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w), hex(b)
+        assert Fraction(g) == bf16_fraction(b)
+
+
+def test_f32_to_bf16_matches_torch_rne():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
+    # exact ties: low 16 bits exactly 0x8000, both parities of the kept bit
+    ties = (rng.integers(0, 2 ** 31, 2000, dtype=np.uint32) & 0x7F7F0000) | 0x8000
+    x = np.concatenate([x, ties.view(np.float32), np.array(
+        [0.0, -0.0, 1e-40, -1e-40, 3.3895314e38, -3.3895314e38, 3.4e38,
+         np.inf, -np.inf, 1.0, 1.00390625, 1.01171875], np.float32)])
+    got = oracle.f32_to_bf16(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_f32_to_bf16_hand_ties():
+    # 1 + 2^-8 lies exactly between bf16 1.0 (even) and 1 + 2^-7 (odd): -> 1.0
+    # 1 + 3*2^-8 lies between 1 + 2^-7 (odd) and 1 + 2^-6 (even): -> 1 + 2^-6
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], np.float32)
+    got = oracle.f32_to_bf16(x)
+    assert list(got) == [0x3F80, 0x3F82, 0xBF80]
+
+
+# --- GEMM -------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 3, 5), (4, 2, 8), (3, 4, 17),
+                                   (4, 4, 64), (1, 3, 33)] +
+                         [(2, 3, k) for k in range(1, 9)])
+def test_gemm_exact_rational(M, N, K):
+    rng = np.random.default_rng(1000 + 7 * M + 13 * N + K)
+    X = rand_bf16((M, K), rng)
+    W = rand_bf16((K, N), rng, 0.05)
+    Y, A = oracle.gemm(X, W)
+    for i in range(M):
+        for j in range(N):
+            exact = sum(bf16_fraction(X[i, k]) * bf16_fraction(W[k, j]) for k in range(K))
+            mag = sum(abs(bf16_fraction(X[i, k]) * bf16_fraction(W[k, j])) for k in range(K))
+            bound = K * 2.0 ** -53 * float(mag)
+            assert abs(Fraction(Y[i, j]) - exact) <= Fraction(bound), (i, j)
+            assert abs(Fraction(A[i, j]) - mag) <= Fraction(bound), (i, j)
+
+
+def test_gemm_integer_exact():
+    # integer-valued bf16 inputs: every partial sum is an integer far below
+    # 2^53, so the fp64 result must equal the int64 product exactly.
+    X = inputs.integer_bf16((37, 1024), -8, 8, 3, 0)
+    W = inputs.integer_bf16((1024, 45), -8, 8, 3, 1)
+    Y, A = oracle.gemm(X, W)
+    Xi = inputs.bf16_bits_to_f32(X).astype(np.int64)
+    Wi = inputs.bf16_bits_to_f32(W).astype(np.int64)
+    np.testing.assert_array_equal(Y, (Xi @ Wi).astype(np.float64))
+    np.testing.assert_array_equal(A, (np.abs(Xi) @ np.abs(Wi)).astype(np.float64))
+
+
+def test_gemm_identity_and_transposition():
+    rng = np.random.default_rng(5)
+    X = rand_bf16((7, 24), rng)
+    eye = inputs.f32_bits_to_bf16_bits(np.eye(24, dtype=np.float32))
+    Y, _ = oracle.gemm(X, eye)
+    np.testing.assert_array_equal(Y, inputs.bf16_bits_to_f32(X).astype(np.float64))
+    # a selection matrix that picks column 3 of X into output column 0 and
+    # column 10 into output column 1 (catches a transposed operand)
+    S = np.zeros((24, 2), np.float32)
+    S[3, 0] = 1.0
+    S[10, 1] = 2.0
+    Y, _ = oracle.gemm(X, inputs.f32_bits_to_bf16_bits(S))
+    xf = inputs.bf16_bits_to_f32(X).astype(np.float64)
+    np.testing.assert_array_equal(Y[:, 0], xf[:, 3])
+    np.testing.assert_array_equal(Y[:, 1], 2 * xf[:, 10])
+
+
+def test_gemm_matches_torch_fp64():
+    X, W = inputs.dense_inputs(33, 640, 70, seed=11)
+    Y, A = oracle.gemm(X, W)
+    ref = torch.from_numpy(inputs.bf16_bits_to_f32(X).astype(np.float64)) @ \
+        torch.from_numpy(inputs.bf16_bits_to_f32(W).astype(np.float64))
+    assert np.all(np.abs(Y - ref.numpy()) <= 1e-12 * A + 1e-300)
+
+
+def test_gemm_empty_k_is_zero():
+    X = np.zeros((3, 0), np.uint16)
+    W = np.zeros((0, 5), np.uint16)
+    Y, A = oracle.gemm(X, W)
+    assert Y.shape == (3, 5) and np.all(Y == 0) and np.all(A == 0)
+
+
+# --- RMSNorm ------------------------------------------------------------------
+
+def test_rmsnorm_pm1_closed_form():
+    H = 4096
+    rng = np.random.default_rng(2)
+    x = inputs.f32_bits_to_bf16_bits(np.where(rng.random((3, H)) < 0.5, -1.0, 1.0).astype(np.float32))
+    _, g = inputs.rmsnorm_inputs(1, H, seed=0)
+    y = oracle.rmsnorm(x, g, 1e-6)
+    scale = 0.999999500000375  # 1/sqrt(1 + 1e-6)
+    want = inputs.bf16_bits_to_f32(g).astype(np.float64) * inputs.bf16_bits_to_f32(x) * scale
+    np.testing.assert_allclose(y, want, rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_constant_row_and_scale_invariance():
+    H = 512
+    c = 3.0
+    x = inputs.f32_bits_to_bf16_bits(np.full((1, H), c, np.float32))
+    g = inputs.f32_bits_to_bf16_bits(np.linspace(0.5, 1.5, H).astype(np.float32))
+    y = oracle.rmsnorm(x, g, 1e-6)
+    gf = inputs.bf16_bits_to_f32(g).astype(np.float64)
+    np.testing.assert_allclose(y[0], gf * c / math.sqrt(c * c + 1e-6), rtol=1e-15)
+    # eps = 0: scaling a row by a power of two leaves the output unchanged
+    x2, g2 = inputs.rmsnorm_inputs(4, H, seed=9)
+    xs = inputs.f32_bits_to_bf16_bits(inputs.bf16_bits_to_f32(x2) * 4.0)
+    np.testing.assert_allclose(oracle.rmsnorm(xs, g2, 0.0), oracle.rmsnorm(x2, g2, 0.0),
+                               rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_matches_torch_fp64():
+    x, g = inputs.rmsnorm_inputs(16, 4096, seed=4)
+    xt = torch.from_numpy(inputs.bf16_bits_to_f32(x).astype(np.float64))
+    gt = torch.from_numpy(inputs.bf16_bits_to_f32(g).astype(np.float64))
+    ref = xt * torch.rsqrt(xt.pow(2).mean(-1, keepdim=True) + 1e-6) * gt
+    np.testing.assert_allclose(oracle.rmsnorm(x, g, 1e-6), ref.numpy(), rtol=1e-13, atol=1e-15)
+
+
+# --- log_softmax --------------------------------------------------------------
+
+def test_log_softmax_constant_row():
+    V = 151936
+    y = oracle.log_softmax(np.full((2, V), 1.75, np.float32))
+    assert np.all(np.abs(y + 11.931214658529285) < 1e-12)
+    assert abs(math.log(V) - 11.931214658529285) < 1e-14
+
+
+def test_log_softmax_two_elements_closed_form():
+    x = np.array([[0.0, math.log(3.0)]], np.float32)
+    y = oracle.log_softmax(x)
+    b = float(np.float32(math.log(3.0)))
+    np.testing.assert_allclose(y[0], [-math.log1p(math.exp(b)), b - math.log1p(math.exp(b))],
+                               rtol=1e-15)
+
+
+def test_log_softmax_normalised_shift_invariant_and_torch():
+    # values on a 2^-10 grid with |x| < 64, so adding 64 is exact in binary32
+    x = np.round(inputs.logits_inputs(3, 20000, seed=1) * 1024.0).astype(np.float32) / np.float32(1024.0)
+    y = oracle.log_softmax(x)
+    assert np.all(np.abs(np.exp(y).sum(axis=1) - 1.0) < 1e-12)
+    y2 = oracle.log_softmax(x + np.float32(64.0))  # exact shift of every element
+    np.testing.assert_allclose(y2, y, atol=1e-12, rtol=0)
+    ref = torch.log_softmax(torch.from_numpy(x.astype(np.float64)), dim=-1).numpy()
+    np.testing.assert_allclose(y, ref, atol=1e-12, rtol=0)
+
+
+# --- mean ---------------------------------------------------------------------
+
+def test_mean_integer_constant_and_numpy():
+    V = 151936
+    xi = inputs.integer_f32((3, V), -8, 8, 5, 4)
+    m = oracle.mean(xi)
+    want = xi.astype(np.int64).sum(axis=1)
+    for r in range(3):
+        assert Fraction(m[r]) == Fraction(int(want[r]), V) or \
+            abs(Fraction(m[r]) - Fraction(int(want[r]), V)) <= Fraction(2.0 ** -52) * abs(Fraction(int(want[r]), V))
+    assert np.all(oracle.mean(np.full((2, 1000), -2.5, np.float32)) == -2.5)
+    x = inputs.logits_inputs(4, V, seed=2)
+    np.testing.assert_allclose(oracle.mean(x), np.mean(x.astype(np.float64), axis=1),
+                               rtol=0, atol=1e-13)
+
+
+# --- the fixed tree and the non-associativity example ------------------------
+
+def test_tree_sum_structure_hand_derived():
+    t24 = float(2 ** 24)
+    # adjacent pairs, level by level.  2^24 + 1 is a tie and rounds to 2^24.
+    # tree: (2^24+1)=2^24, (1+1)=2, 2^24+2 exact; (-2^24+0)+(0+0) = -2^24 -> 2
+    # left fold: 2^24, 2^24, 2^24, 0, 0, 0, 0 -> 0
+    P = np.array([t24, 1, 1, 1, -t24, 0, 0, 0], np.float32).reshape(8, 1)
+    assert oracle.tree_sum_f32(P)[0] == 2.0
+    assert oracle.fold_sum_f32(P[:, 0]) == 0.0
+    # pairing across halves ((p0+p4)+(p1+p5)..) would give (2^24-2^24)+... = 3;
+    # the tree gives ((p0+p1)+(p2+p3)) + ... = (2^24 + 2) - 2^24 = 2.
+    # S = 4 on the first half: (2^24+1)+(1+1) = 2^24 + 2
+    assert oracle.tree_sum_f32(P[:4])[0] == t24 + 2
+    # S = 2 is one IEEE addition; S = 1 the identity
+    assert oracle.tree_sum_f32(P[:2])[0] == t24
+    assert oracle.tree_sum_f32(P[:1])[0] == t24
+    # level order: ((a+b)+(c+d)) with a=2^24, b=-2^24, c=1, d=2^-30
+    # -> 0 + (1 + 2^-30 rounds to 1) = 1
+    Q = np.array([t24, -t24, 1.0, 2.0 ** -30], np.float32).reshape(4, 1)
+    assert oracle.tree_sum_f32(Q)[0] == 1.0
+    with pytest.raises(ValueError):
+        oracle.tree_sum_f32(np.zeros((3, 1), np.float32))
+
+
+def test_nonassociativity_example_from_pages():
+    rows = []
+    with open(os.path.join(GOLDEN, "nonassoc_fp32.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            expr, r32, r64 = [s.strip() for s in line.split("|")]
+            rows.append((expr, float(r32), float(r64)))
+    one, big = np.float32(1.0), np.float32(1e8)
+    f32 = {
+        "(1e8 + 1) - 1e8": (big + one) - big,
+        "1e8 + (1 - 1e8)": big + (one - big),
+        "(1 + 1e8) - 1e8": (one + big) - big,
+        "1 + (1e8 - 1e8)": one + (big - big),
+    }
+    f64 = {
+        "(1e8 + 1) - 1e8": (1e8 + 1.0) - 1e8,
+        "1e8 + (1 - 1e8)": 1e8 + (1.0 - 1e8),
+        "(1 + 1e8) - 1e8": (1.0 + 1e8) - 1e8,
+        "1 + (1e8 - 1e8)": 1.0 + (1e8 - 1e8),
+    }
+    assert len(rows) == 4
+    for expr, r32, r64 in rows:
+        assert float(f32[expr]) == r32, expr
+        assert f64[expr] == r64, expr
+    # the page's literal pair does NOT differ in binary32 (both are 0) ...
+    assert f32["(1e8 + 1) - 1e8"] == f32["1e8 + (1 - 1e8)"] == 0.0
+    # ... while the regrouped pair does: order matters in binary32
+    assert f32["(1 + 1e8) - 1e8"] != f32["1 + (1e8 - 1e8)"]
+    # "Order A / Order B for merging results": the oracle's fold over the
+    # partials in two orders gives 0 and 1; fp64 gives 1 for every order
+    assert oracle.fold_sum_f32([1e8, 1, -1e8]) == 0.0
+    assert oracle.fold_sum_f32([1e8, -1e8, 1]) == 1.0
+    X = inputs.f32_bits_to_bf16_bits(np.array([[1.0, 1.0, 1.0]], np.float32))
+    # 1e8 is not a bf16 value; use 2^27 (same effect: spacing 16 > 1)
+    W = inputs.f32_bits_to_bf16_bits(np.array([[2.0 ** 27], [1.0], [-2.0 ** 27]], np.float32))
+    Y, _ = oracle.gemm(X, W)
+    assert Y[0, 0] == 1.0
