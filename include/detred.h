@@ -1,0 +1,226 @@
+/*
+ * detred.h -- deterministic, batch-invariant and tensor-parallel-invariant
+ * reductions for MI355X (gfx950).
+ *
+ * C ABI.  All tensor arguments are DEVICE pointers allocated and owned by the
+ * caller; the library keeps no pointer after a call returns and allocates no
+ * device memory on any compute call.  bf16 tensors are passed as their 16-bit
+ * patterns (uint16_t).  Every matrix is row-major with an explicit leading
+ * dimension (elements between the starts of consecutive rows).
+ *
+ * Calls are asynchronous on the given stream (a hipStream_t passed as void*,
+ * NULL = the null stream).  Validation is synchronous: a return value other
+ * than DETRED_OK means nothing was launched.
+ *
+ * Which operations and why
+ * ------------------------
+ * Split-K parallelises a matrix product over its reduction dimension K: K is
+ * cut into slices, each slice produces an fp32 partial result, and the
+ * partials are summed.  Summing them with floating-point atomics makes the
+ * order, and so the rounding, depend on timing ("Reproducible LoRA Inference
+ * Through Deterministic Split-K Reduction", Highlights and Q&A); summing them
+ * in a fixed order removes that.  Using one hierarchical binary tree for the
+ * partial sums inside a GPU and across GPUs makes the bits independent of the
+ * tensor-parallel size as well (arXiv 2511.17826, "Deterministic Inference
+ * across Tensor Parallel Sizes...", Abstract).  Row reductions such as RMSNorm
+ * must likewise reduce each row in an order that does not depend on the batch
+ * ("Restoring AI Reproducibility: Thinking Machines Lab's Challenge to
+ * Overcome Nondeterminism", sections 2-2 to 3-2); mm, addmm, log_softmax and
+ * mean are the operations the "Batch Invariant Ops" project makes batch
+ * invariant (Highlighted Details).
+ *
+ * The canonical reduction of a product (every GEMM entry point)
+ * -------------------------------------------------------------
+ * For a reduction length K the library fixes, from K alone:
+ *   P  = 8 chunks if K >= 256 and K % 256 == 0, else P = 1;
+ *   Kc = K / P, chunk c covers k in [c*Kc, (c+1)*Kc).
+ * Output element (i,j) is
+ *   chunk_c(i,j) = a chain of v_mfma_f32_16x16x32_bf16 steps over the chunk's
+ *                  k in increasing order, starting from +0.0f, 32 k per step
+ *                  (a step that runs past K uses exact zeros for the missing
+ *                  k; this only happens when P = 1);
+ *   Y(i,j)       = the fixed binary tree over the P chunk values:
+ *                  ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)), one binary32
+ *                  round-to-nearest-even addition per node.
+ * A split into S slices (S | P) gives slice s the chunks
+ * [s*P/S, (s+1)*P/S), which form a complete subtree; the slices' partials are
+ * then combined by the top log2(S) levels of the same tree.  The same holds
+ * for T tensor-parallel shards.  Hence Y's bits do not depend on the batch
+ * size M, on a row's position in the batch, on S, on T, on the tile shape, on
+ * the stream or on replay.  atomic_splitk_gemm is the only exception: it is
+ * the nondeterministic control.
+ *
+ * Requirements shared by the GEMM entry points (else the status shown):
+ *   M, N, K >= 0; ldx >= K, ldw >= N, ldy >= N                   (EINVAL)
+ *   X, W, Y 16-byte aligned; ldx, ldw multiples of 8; ldy of 4    (EINVAL)
+ *   K % 8 == 0 and N % 8 == 0                                  (EUNSUPPORTED)
+ *   split_k / tp_shards in {1,2,4,8} and <= P                  (EUNSUPPORTED)
+ * M == 0 or N == 0 launches nothing and returns DETRED_OK; K == 0 writes
+ * +0.0f to Y.  Y must not overlap X, W or the workspace.
+ */
+#ifndef DETRED_H
+#define DETRED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DETRED_OK = 0,
+    DETRED_EINVAL = 1,       /* null/misaligned pointer, bad dims or ld   */
+    DETRED_EUNSUPPORTED = 2, /* valid but outside what the kernels cover  */
+    DETRED_EWORKSPACE = 3,   /* workspace missing or too small            */
+    DETRED_EHIP = 4          /* the HIP runtime reported an error         */
+} detred_status;
+
+typedef void *detred_stream; /* hipStream_t; NULL = null stream */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *detred_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int detred_version(void);
+
+/*
+ * The locked policy for a product with N output columns and reduction
+ * length K (it never depends on M).  Writes, where the pointer is non-NULL:
+ *   chunks   = P (1 or 8) and chunk_k = Kc;
+ *   tile_m, tile_n = the workgroup output tile;
+ *   default_split  = the split used when split_k = 0 is passed.
+ * Returns EINVAL for N < 0 or K < 0.
+ */
+int detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
+                  int *tile_n, int *default_split);
+
+/*
+ * Workspace size in bytes that det_splitk_gemm (split_k = S) or tree_tp_gemm
+ * (tp_shards = S) needs for an M x N output with reduction length K:
+ * S fp32 partial arrays of M*N elements plus one 32-bit counter per output
+ * tile, rounded up to 256 bytes.  0 when S == 1 (no workspace is used).
+ * Returns 0 for invalid arguments as well.
+ */
+size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards);
+
+/*
+ * Zero a workspace's counters (the whole buffer) on stream s.  Call once
+ * after allocating a workspace; every det_splitk_gemm call leaves the
+ * counters at zero again when it completes.  One workspace serves one call
+ * in flight at a time.
+ */
+int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
+
+/*
+ * Deterministic split-K product Y[M,N] (fp32) = X[M,K] W[K,N] (bf16), the
+ * fixed-order split-K of the split-K paper (Highlights, Q&A) with the
+ * canonical tree above.  split_k = S in {1,2,4,8} (S <= P), or 0 for the
+ * policy's default.  With S > 1 each slice writes its fp32 partial into the
+ * workspace as S row-major [M][N] arrays (ld N) at byte offset 0, the last
+ * slice of every output tile to finish adds the S partials in the fixed tree
+ * order and writes Y; one launch in total.  ws may be NULL when S == 1.
+ * ws must be 256-byte aligned and at least detred_gemm_workspace_bytes()
+ * large (EWORKSPACE otherwise), and its counters zero (detred_workspace_init).
+ * The bits of Y do not depend on S.
+ */
+int det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                    float *Y, int ldy, int M, int N, int K, int split_k,
+                    void *ws, size_t ws_bytes, detred_stream s);
+
+/*
+ * The nondeterministic control: the same slice products as det_splitk_gemm,
+ * but Y is zero-filled on the stream and every slice adds its partial into Y
+ * with fp32 atomic additions, so the summation order follows the order in
+ * which slices finish (split-K paper, Q&A: partial results combined with
+ * floating-point atomic additions).  split_k as above (0 = default).  The
+ * zero fill is part of the call.  Results agree with the oracle to the same
+ * tolerance but are not bit-reproducible.
+ */
+int atomic_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                       float *Y, int ldy, int M, int N, int K, int split_k,
+                       detred_stream s);
+
+/*
+ * Tree-based TP-invariant product on one GPU (TBIK, arXiv 2511.17826,
+ * Abstract): K is cut into tp_shards = T contiguous shards (T in {1,2,4,8},
+ * T <= P); shard t reduces chunks [t*P/T, (t+1)*P/T) to its subtree root and
+ * writes it to its own fp32 [M][N] buffer (the value rank t of a T-way
+ * row-parallel group would hold before the all-reduce); the buffers are then
+ * added by the top log2(T) levels of the same tree into Y (the step the
+ * inter-GPU reduction performs).  Two launches for T > 1, one for T == 1.
+ * ws: T*M*N fp32 shard buffers (detred_gemm_workspace_bytes(M,N,K,T));
+ * may be NULL when T == 1.  Y's bits equal det_splitk_gemm's for every T.
+ */
+int tree_tp_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                 float *Y, int ldy, int M, int N, int K, int tp_shards,
+                 void *ws, size_t ws_bytes, detred_stream s);
+
+/*
+ * One shard of tree_tp_gemm at its own share shape: what rank t of a
+ * T-way row-parallel group computes locally.  Xt is the rank's [M, Kt]
+ * activation shard, Wt its [Kt, N] weight shard, Kt = K / T, and Pt
+ * (fp32 [M][N], ld ldp) receives the root of the shard's subtree: its
+ * P/T chunks of width K/8 each.  Requires Kt*T to satisfy the P = 8 rule
+ * (Kt*T >= 256, Kt*T % 256 == 0) when T > 1.
+ */
+int tree_tp_shard_gemm(const uint16_t *Xt, int ldx, const uint16_t *Wt,
+                       int ldw, float *Pt, int ldp, int M, int N, int Kt,
+                       int tp_shards, detred_stream s);
+
+/*
+ * The fixed binary tree over `count` fp32 arrays of n elements each
+ * (count in {1,2,4,8}): parts + i*part_stride (elements) is array i;
+ * Y[e] = ((p0+p1)+(p2+p3))+... as in the canonical tree's top levels.
+ * parts and Y 16-byte aligned, part_stride and n multiples of 4.
+ * Y may not overlap the parts.
+ */
+int tree_combine_f32(const float *parts, size_t part_stride, int count,
+                     float *Y, size_t n, detred_stream s);
+
+/*
+ * The explicit binary32 -> bf16 cast (round to nearest, ties to even) that
+ * turns the fp32 LoRA shrink output into the bf16 input of the expand
+ * (split-K paper, Q&A: shrink, then expand).  n elements; x, y 16-byte
+ * aligned, n % 8 == 0.  NaN stays NaN.
+ */
+int detred_f32_to_bf16(const float *x, uint16_t *y, size_t n, detred_stream s);
+
+/*
+ * Batch-invariant RMSNorm (Thinking Machines article, 2-3 and 3-1: each row
+ * handled by one workgroup and reduced in one fixed order):
+ *   y[r][j] = (x[r][j] * inv) * gamma[j],  inv = 1 / sqrt(ss/hidden + eps),
+ *   ss = sum_j x[r][j]^2 in binary32 in a fixed order that depends only on
+ *   hidden.
+ * x bf16 [rows][hidden], gamma bf16 [hidden], y fp32 [rows][hidden], all
+ * contiguous and 16-byte aligned; hidden % 8 == 0, 0 < hidden <= 65536
+ * (EUNSUPPORTED otherwise).  rows == 0 launches nothing.
+ */
+int inv_rmsnorm(const uint16_t *x, const uint16_t *gamma, float *y, int rows,
+                int hidden, float eps, detred_stream s);
+
+/*
+ * Batch-invariant log_softmax over the last dimension (Batch Invariant Ops,
+ * Highlighted Details): y[r][j] = (x[r][j] - m) - log(s), with m the row
+ * maximum and s = sum_j exp(x[r][j] - m), both reduced by one workgroup per
+ * row in a fixed order that depends only on cols.  x, y fp32 [rows][cols]
+ * contiguous, 16-byte aligned, cols % 4 == 0 and cols > 0 (EUNSUPPORTED
+ * otherwise).  x and y may be the same buffer.
+ */
+int inv_log_softmax(const float *x, float *y, int rows, int cols,
+                    detred_stream s);
+
+/*
+ * Batch-invariant mean over the last dimension (Batch Invariant Ops,
+ * Highlighted Details): y[r] = (sum_j x[r][j]) / cols, the sum in binary32
+ * in a fixed order that depends only on cols, then one IEEE division.
+ * x fp32 [rows][cols] contiguous, 16-byte aligned, cols % 4 == 0, cols > 0;
+ * y fp32 [rows].
+ */
+int inv_mean(const float *x, float *y, int rows, int cols, detred_stream s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETRED_H */

@@ -1,0 +1,335 @@
+// C-ABI layer of libdetred: argument checks, the locked policy, workspace
+// layout and kernel launches.  Declarations and the contract of every entry
+// point are in include/detred.h.
+#include "detred.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+using namespace detred;
+
+namespace {
+
+constexpr int kChunks = 8;          // chunks of K when K allows them
+constexpr int kChunkGranule = 256;  // K must be a multiple of this for 8 chunks
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+bool pow2_le8(int v) { return v == 1 || v == 2 || v == 4 || v == 8; }
+
+int chunk_count(int K) { return (K >= kChunkGranule && K % kChunkGranule == 0) ? kChunks : 1; }
+
+// The locked policy.  It is a function of (N, K) only, never of M, of the
+// split or of the shard count: the tile decides speed, the chunk tree
+// decides the bits.
+struct Policy {
+    int P, Kc, tile, bm, bn, default_split;
+};
+
+Policy policy_for(int N, int K)
+{
+    Policy p;
+    p.P = chunk_count(K);
+    p.Kc = K / p.P;
+    if (N <= 16) {
+        p.tile = TILE_S16;
+        p.default_split = p.P;   // skinny outputs: parallelise over K
+    } else if (N <= 64 || p.P == 1) {
+        p.tile = TILE_M64;
+        p.default_split = N <= 64 ? p.P : 1;
+    } else {
+        p.tile = TILE_L128;
+        p.default_split = 1;
+    }
+    tile_shape(p.tile, &p.bm, &p.bn);
+    return p;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t partial_bytes(int M, int N, int S) { return round_up((size_t)S * M * N * sizeof(float), 256); }
+
+size_t counter_bytes(const Policy& p, int M, int N)
+{
+    const size_t tm = (size_t)(M + p.bm - 1) / p.bm, tn = (size_t)(N + p.bn - 1) / p.bn;
+    return round_up(tm * tn * sizeof(unsigned), 256);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DETRED_OK : DETRED_EHIP; }
+
+// Checks shared by the GEMM entry points.
+int check_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* Y, int ldy,
+               int M, int N, int K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return DETRED_EINVAL;
+    if (ldx < K || ldw < N || ldy < N || ldx < 0 || ldw < 0 || ldy < 0)
+        return DETRED_EINVAL;
+    if (M == 0 || N == 0)
+        return DETRED_OK;
+    if (!Y || !aligned16(Y) || (ldy % 4) != 0)
+        return DETRED_EINVAL;
+    if (K > 0) {
+        if (!X || !W || !aligned16(X) || !aligned16(W) || (ldx % 8) != 0 || (ldw % 8) != 0)
+            return DETRED_EINVAL;
+    }
+    if ((K % 8) != 0 || (N % 8) != 0)
+        return DETRED_EUNSUPPORTED;
+    return DETRED_OK;
+}
+
+GemmArgs make_args(const Policy& p, const uint16_t* X, int ldx, const uint16_t* W, int ldw,
+                   float* Y, int ldy, int M, int N, int K, int slices)
+{
+    GemmArgs g;
+    g.X = X;
+    g.ldx = ldx;
+    g.W = W;
+    g.ldw = ldw;
+    g.Y = Y;
+    g.ldy = ldy;
+    g.out_z_stride = 0;
+    g.part = nullptr;
+    g.counters = nullptr;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.Kc = p.Kc;
+    g.slices = slices;
+    g.tiles_m = (M + p.bm - 1) / p.bm;
+    g.tiles_n = (N + p.bn - 1) / p.bn;
+    return g;
+}
+
+// Resolve split_k / tp_shards against the policy; 0 means the default.
+int resolve_split(const Policy& p, int split, int* out)
+{
+    if (split == 0)
+        split = p.default_split;
+    if (!pow2_le8(split) || split > p.P)
+        return DETRED_EUNSUPPORTED;
+    *out = split;
+    return DETRED_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* detred_status_string(int status)
+{
+    switch (status) {
+    case DETRED_OK: return "DETRED_OK";
+    case DETRED_EINVAL: return "DETRED_EINVAL: invalid argument";
+    case DETRED_EUNSUPPORTED: return "DETRED_EUNSUPPORTED: shape or split not supported";
+    case DETRED_EWORKSPACE: return "DETRED_EWORKSPACE: workspace missing or too small";
+    case DETRED_EHIP: return "DETRED_EHIP: HIP runtime error";
+    }
+    return "DETRED_UNKNOWN_STATUS";
+}
+
+int detred_version(void) { return 100; }
+
+int detred_policy(int N, int K, int* chunks, int* chunk_k, int* tile_m, int* tile_n,
+                  int* default_split)
+{
+    if (N < 0 || K < 0)
+        return DETRED_EINVAL;
+    const Policy p = policy_for(N, K);
+    if (chunks) *chunks = p.P;
+    if (chunk_k) *chunk_k = p.Kc;
+    if (tile_m) *tile_m = p.bm;
+    if (tile_n) *tile_n = p.bn;
+    if (default_split) *default_split = p.default_split;
+    return DETRED_OK;
+}
+
+size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards)
+{
+    if (M < 0 || N < 0 || K < 0 || !pow2_le8(split_or_shards))
+        return 0;
+    if (split_or_shards == 1)
+        return 0;
+    const Policy p = policy_for(N, K);
+    return partial_bytes(M, N, split_or_shards) + counter_bytes(p, M, N);
+}
+
+int detred_workspace_init(void* ws, size_t ws_bytes, detred_stream s)
+{
+    if (ws_bytes == 0)
+        return DETRED_OK;
+    if (!ws)
+        return DETRED_EINVAL;
+    return hip_status(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)s));
+}
+
+int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
+                    int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+{
+    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = policy_for(N, K);
+    int S = 0;
+    if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
+        return st;
+    hipStream_t hs = (hipStream_t)s;
+    if (K == 0)
+        return hip_status(launch_fill_zero(Y, ldy, M, N, hs));
+    GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
+    if (S == 1)
+        return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
+    const size_t need = partial_bytes(M, N, S) + counter_bytes(p, M, N);
+    if (!ws || !aligned256(ws) || ws_bytes < need)
+        return DETRED_EWORKSPACE;
+    g.part = (float*)ws;
+    g.counters = (unsigned*)((char*)ws + partial_bytes(M, N, S));
+    return hip_status(launch_slice_gemm(p.tile, EPI_COMBINE, g, p.P / S, hs));
+}
+
+int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
+                       int M, int N, int K, int split_k, detred_stream s)
+{
+    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = policy_for(N, K);
+    int S = 0;
+    if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
+        return st;
+    hipStream_t hs = (hipStream_t)s;
+    hipError_t e = launch_fill_zero(Y, ldy, M, N, hs);
+    if (e != hipSuccess || K == 0)
+        return hip_status(e);
+    GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
+    return hip_status(launch_slice_gemm(p.tile, EPI_ATOMIC, g, p.P / S, hs));
+}
+
+int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
+                 int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes, detred_stream s)
+{
+    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = policy_for(N, K);
+    if (!pow2_le8(tp_shards) || tp_shards > p.P)
+        return DETRED_EUNSUPPORTED;
+    const int T = tp_shards;
+    hipStream_t hs = (hipStream_t)s;
+    if (K == 0)
+        return hip_status(launch_fill_zero(Y, ldy, M, N, hs));
+    GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, T);
+    if (T == 1)
+        return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
+    if (!ws || !aligned256(ws) || ws_bytes < partial_bytes(M, N, T))
+        return DETRED_EWORKSPACE;
+    // phase 1: every shard writes its subtree root to its own buffer
+    g.Y = (float*)ws;
+    g.ldy = N;
+    g.out_z_stride = (long)M * N;
+    hipError_t e = launch_slice_gemm(p.tile, EPI_STORE, g, p.P / T, hs);
+    if (e != hipSuccess)
+        return DETRED_EHIP;
+    // phase 2: the top log2(T) tree levels (the cross-rank reduction)
+    if (ldy == N)
+        return hip_status(launch_tree_combine((const float*)ws, (size_t)M * N, T, Y,
+                                              (size_t)M * N, hs));
+    for (int r = 0; r < M; ++r) {  // strided output: one combine per row
+        e = launch_tree_combine((const float*)ws + (size_t)r * N, (size_t)M * N, T,
+                                Y + (size_t)r * ldy, (size_t)N, hs);
+        if (e != hipSuccess)
+            return DETRED_EHIP;
+    }
+    return DETRED_OK;
+}
+
+int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, float* Pt,
+                       int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+{
+    if (!pow2_le8(tp_shards) || Kt < 0)
+        return DETRED_EINVAL;
+    const long Kl = (long)Kt * tp_shards;
+    if (Kl > 0x7fffffffL)
+        return DETRED_EINVAL;
+    const int K = (int)Kl;
+    int st = check_gemm(Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = policy_for(N, K);
+    if (tp_shards > p.P)
+        return DETRED_EUNSUPPORTED;
+    hipStream_t hs = (hipStream_t)s;
+    if (Kt == 0)
+        return hip_status(launch_fill_zero(Pt, ldp, M, N, hs));
+    // the shard's own K range is chunks [0, P/T) of width K/P
+    GemmArgs g = make_args(p, Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, 1);
+    return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
+}
+
+int tree_combine_f32(const float* parts, size_t part_stride, int count, float* Y, size_t n,
+                     detred_stream s)
+{
+    if (!pow2_le8(count))
+        return DETRED_EUNSUPPORTED;
+    if (n == 0)
+        return DETRED_OK;
+    if (!parts || !Y || !aligned16(parts) || !aligned16(Y) || (n % 4) != 0 ||
+        (part_stride % 4) != 0 || (count > 1 && part_stride < n))
+        return DETRED_EINVAL;
+    return hip_status(launch_tree_combine(parts, part_stride, count, Y, n, (hipStream_t)s));
+}
+
+int detred_f32_to_bf16(const float* x, uint16_t* y, size_t n, detred_stream s)
+{
+    if (n == 0)
+        return DETRED_OK;
+    if (!x || !y || !aligned16(x) || !aligned16(y))
+        return DETRED_EINVAL;
+    if ((n % 8) != 0)
+        return DETRED_EUNSUPPORTED;
+    return hip_status(launch_cast_bf16(x, y, n, (hipStream_t)s));
+}
+
+int inv_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows, int hidden,
+                float eps, detred_stream s)
+{
+    if (rows < 0 || hidden < 0)
+        return DETRED_EINVAL;
+    if (rows == 0)
+        return DETRED_OK;
+    if (!x || !gamma || !y || !aligned16(x) || !aligned16(gamma) || !aligned16(y))
+        return DETRED_EINVAL;
+    if (hidden == 0 || hidden % 8 != 0 || hidden > 65536)
+        return DETRED_EUNSUPPORTED;
+    return hip_status(launch_rmsnorm(x, gamma, y, rows, hidden, eps, (hipStream_t)s));
+}
+
+int inv_log_softmax(const float* x, float* y, int rows, int cols, detred_stream s)
+{
+    if (rows < 0 || cols < 0)
+        return DETRED_EINVAL;
+    if (rows == 0)
+        return DETRED_OK;
+    if (!x || !y || !aligned16(x) || !aligned16(y))
+        return DETRED_EINVAL;
+    if (cols == 0 || cols % 4 != 0)
+        return DETRED_EUNSUPPORTED;
+    return hip_status(launch_log_softmax(x, y, rows, cols, (hipStream_t)s));
+}
+
+int inv_mean(const float* x, float* y, int rows, int cols, detred_stream s)
+{
+    if (rows < 0 || cols < 0)
+        return DETRED_EINVAL;
+    if (rows == 0)
+        return DETRED_OK;
+    if (!x || !y || !aligned16(x))
+        return DETRED_EINVAL;
+    if (cols == 0 || cols % 4 != 0)
+        return DETRED_EUNSUPPORTED;
+    return hip_status(launch_mean(x, y, rows, cols, (hipStream_t)s));
+}
+
+}  // extern "C"

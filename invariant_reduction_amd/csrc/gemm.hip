@@ -1,0 +1,554 @@
+// Slice GEMM for gfx950: bf16 MFMA products whose K reduction follows one
+// fixed chunk tree, plus the tree combine, the atomic control and the
+// helpers the GEMM entry points need.
+//
+// The reduction of output element (i,j) (see include/detred.h):
+//   * K is cut into P chunks (P = 8, or 1 for short/odd K) of width Kc;
+//   * a chunk is one chain of v_mfma_f32_16x16x32_bf16 steps over its k in
+//     increasing order, starting from +0;
+//   * the P chunk values are added by the binary tree
+//     ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)).
+// A workgroup owns one output tile and one slice (CPS consecutive chunks,
+// a complete subtree).  It folds its chunks with a binary counter: after
+// chunk c, the running value is added to the stored left siblings for every
+// trailing one bit of c, which evaluates exactly the subtree above.  The
+// slices' roots are then added by the top levels of the same tree, either
+// by the last workgroup of a tile to finish (det), by a separate combine
+// launch (tensor-parallel shards) or by fp32 atomics (the control).
+//
+// Sources: "Reproducible LoRA Inference Through Deterministic Split-K
+// Reduction" (Highlights; Q&A: split-K partials combined by atomics versus
+// in a fixed order); arXiv 2511.17826 "Deterministic Inference across Tensor
+// Parallel Sizes..." (Abstract: one hierarchical binary tree for intra- and
+// inter-GPU reduction orders).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace detred {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup tile description.  Waves form a WAVES_M x WAVES_N grid; each
+// wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 MFMA tiles.  K is
+// staged through LDS in BK-wide blocks.  In LDS, A is kept [m][k] and B
+// transposed to [n][k] so that both MFMA operands are read as 16 contiguous
+// bytes per lane.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int KSTEPS = BK / 32;
+    static constexpr int LDK = BK + 8;  // LDS row length in bf16 (16-byte pad)
+    static constexpr int A_ELEMS = BM * LDK, B_ELEMS = BN * LDK;
+    static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
+    static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * 2;
+    static constexpr int A_VECS = BM * BK / 8;             // 16-byte vectors
+    static constexpr int A_PER_THREAD = (A_VECS + THREADS - 1) / THREADS;
+    static constexpr int B_SUBS = (BK / 4) * (BN / 8);     // 4k x 8n blocks
+    static constexpr int B_PER_THREAD = (B_SUBS + THREADS - 1) / THREADS;
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be 16-aligned");
+    static_assert(BK % 32 == 0, "K block must hold whole MFMA steps");
+};
+
+using TileS16 = Tile<64, 16, 4, 1, 64>;
+using TileM64 = Tile<64, 64, 2, 2, 64>;
+using TileL128 = Tile<128, 128, 2, 2, 64>;
+
+template <int N>
+struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };
+template <>
+struct Log2<1> { static constexpr int value = 0; };
+
+// Whether the top level of an 8-chunk subtree is parked in LDS (large wave
+// tiles only, where four register copies of the accumulators do not fit).
+template <class T, int CPS>
+struct TopLevelInLds {
+    static constexpr bool value = (CPS == 8) && (T::FM * T::FN >= 16);
+};
+
+template <class T, int CPS>
+constexpr int lds_bytes()
+{
+    return T::LDS_BYTES + (TopLevelInLds<T, CPS>::value ? T::WAVES * T::FM * T::FN * 64 * 16 : 0);
+}
+
+// Map the hardware workgroup id to a logical one so that consecutive logical
+// tiles land on the same XCD (workgroups are dispatched round-robin over the
+// 8 XCDs, each with its own L2).
+__device__ __forceinline__ int xcd_remap(int b, int G)
+{
+    const int xcd = b & 7, local = b >> 3;
+    const int per = G >> 3, rem = G & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+template <class T>
+struct Prefetch {
+    uint4 a[T::A_PER_THREAD];
+    uint4 b[T::B_PER_THREAD][4];
+};
+
+// Global -> registers for one K block [kb, kb+BK) clipped to the chunk end ce.
+template <class T>
+__device__ __forceinline__ void load_block(Prefetch<T>& pf, const GemmArgs& g,
+                                           int row0, int col0, int kb, int ce, int tid)
+{
+#pragma unroll
+    for (int i = 0; i < T::A_PER_THREAD; ++i) {
+        const int v = tid + i * T::THREADS;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (v < T::A_VECS) {
+            const int r = v / (T::BK / 8), kv = v % (T::BK / 8);
+            const int grow = row0 + r, gk = kb + 8 * kv;
+            if (grow < g.M && gk < ce)
+                val = *reinterpret_cast<const uint4*>(g.X + (size_t)grow * g.ldx + gk);
+        }
+        pf.a[i] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_THREAD; ++i) {
+        const int s = tid + i * T::THREADS;
+        const int kq = s / (T::BN / 8), nq = s % (T::BN / 8);
+        const int n = col0 + 8 * nq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint4 val = make_uint4(0, 0, 0, 0);
+            const int k = kb + 4 * kq + j;
+            if (s < T::B_SUBS && k < ce && n < g.N)
+                val = *reinterpret_cast<const uint4*>(g.W + (size_t)k * g.ldw + n);
+            pf.b[i][j] = val;
+        }
+    }
+}
+
+// Registers -> LDS stage.  A is copied as is; each 4k x 8n block of B is
+// transposed to 8 rows (one per n) of 4 consecutive k.
+template <class T>
+__device__ __forceinline__ void store_block(const Prefetch<T>& pf, uint16_t* stage, int tid)
+{
+    uint16_t* sA = stage;
+    uint16_t* sB = stage + T::A_ELEMS;
+#pragma unroll
+    for (int i = 0; i < T::A_PER_THREAD; ++i) {
+        const int v = tid + i * T::THREADS;
+        if (v < T::A_VECS) {
+            const int r = v / (T::BK / 8), kv = v % (T::BK / 8);
+            *reinterpret_cast<uint4*>(sA + r * T::LDK + 8 * kv) = pf.a[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_THREAD; ++i) {
+        const int s = tid + i * T::THREADS;
+        if (s < T::B_SUBS) {
+            const int kq = s / (T::BN / 8), nq = s % (T::BN / 8);
+            const uint32_t r0[4] = {pf.b[i][0].x, pf.b[i][0].y, pf.b[i][0].z, pf.b[i][0].w};
+            const uint32_t r1[4] = {pf.b[i][1].x, pf.b[i][1].y, pf.b[i][1].z, pf.b[i][1].w};
+            const uint32_t r2[4] = {pf.b[i][2].x, pf.b[i][2].y, pf.b[i][2].z, pf.b[i][2].w};
+            const uint32_t r3[4] = {pf.b[i][3].x, pf.b[i][3].y, pf.b[i][3].z, pf.b[i][3].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                // column 2d: low halves; column 2d+1: high halves
+                uint2 even, odd;
+                even.x = (r0[d] & 0xffffu) | (r1[d] << 16);
+                even.y = (r2[d] & 0xffffu) | (r3[d] << 16);
+                odd.x = (r0[d] >> 16) | (r1[d] & 0xffff0000u);
+                odd.y = (r2[d] >> 16) | (r3[d] & 0xffff0000u);
+                *reinterpret_cast<uint2*>(sB + (8 * nq + 2 * d) * T::LDK + 4 * kq) = even;
+                *reinterpret_cast<uint2*>(sB + (8 * nq + 2 * d + 1) * T::LDK + 4 * kq) = odd;
+            }
+        }
+    }
+}
+
+// MFMA over the first nks 32-wide k steps of one LDS stage, increasing k.
+// FULL: every 16x16 tile of the wave is inside M and N; otherwise tiles
+// past fm_act / fn_act are skipped (rows and columns are independent, so
+// skipping them never changes a kept element).
+template <class T, bool FULL>
+__device__ __forceinline__ void mma_block(f32x4 (&acc)[T::FM][T::FN], const uint16_t* stage,
+                                          int nks, int wm, int wn, int lane,
+                                          int fm_act, int fn_act)
+{
+    const uint16_t* sA = stage + (wm * T::TM + (lane & 15)) * T::LDK + 8 * (lane >> 4);
+    const uint16_t* sB = stage + T::A_ELEMS + (wn * T::TN + (lane & 15)) * T::LDK + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < T::KSTEPS; ++ks) {
+        if (ks < nks) {
+            bf16x8 af[T::FM], bfr[T::FN];
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm)
+                if (FULL || fm < fm_act)
+                    af[fm] = *reinterpret_cast<const bf16x8*>(sA + fm * 16 * T::LDK + 32 * ks);
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn)
+                if (FULL || fn < fn_act)
+                    bfr[fn] = *reinterpret_cast<const bf16x8*>(sB + fn * 16 * T::LDK + 32 * ks);
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < T::FN; ++fn)
+                    if (FULL || (fm < fm_act && fn < fn_act))
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+        }
+    }
+}
+
+// Element (r, c) of 16x16 tile (fm, fn) as held by a lane of the
+// v_mfma_f32_16x16x32_bf16 result: register q holds row 4*(lane/16)+q,
+// column lane%16.
+template <class T>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[T::FM][T::FN], float* out,
+                                           long ld, int M, int N, int wrow0, int wcol0,
+                                           int lane, bool atomic)
+{
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = wrow0 + fm * 16 + 4 * (lane >> 4) + q;
+                const int col = wcol0 + fn * 16 + (lane & 15);
+                if (row < M && col < N) {
+                    float* p = out + (size_t)row * ld + col;
+                    if (atomic)
+                        unsafeAtomicAdd(p, acc[fm][fn][q]);
+                    else
+                        *p = acc[fm][fn][q];
+                }
+            }
+}
+
+template <class T, int CPS, int EPI>
+__global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    __shared__ int s_last;
+    constexpr int LOG = Log2<CPS>::value;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+
+    // logical id -> (slice z, tile column tn, tile row tm); tile rows fastest
+    const int G = g.tiles_m * g.tiles_n * g.slices;
+    const int lid = xcd_remap(blockIdx.x, G);
+    const int tiles = g.tiles_m * g.tiles_n;
+    const int z = lid / tiles;
+    const int tl = lid % tiles;
+    const int tn = tl / g.tiles_m, tm = tl % g.tiles_m;
+    const int row0 = tm * T::BM, col0 = tn * T::BN;
+
+    const int wrow0 = row0 + wm * T::TM, wcol0 = col0 + wn * T::TN;
+    int fm_act = (g.M - wrow0 + 15) / 16;
+    fm_act = fm_act < 0 ? 0 : (fm_act > T::FM ? T::FM : fm_act);
+    int fn_act = (g.N - wcol0 + 15) / 16;
+    fn_act = fn_act < 0 ? 0 : (fn_act > T::FN ? T::FN : fn_act);
+    const bool full = (fm_act == T::FM) && (fn_act == T::FN);
+
+    const int kslice = z * CPS * g.Kc;            // first k of this slice
+    const int nb = (g.Kc + T::BK - 1) / T::BK;     // K blocks per chunk
+    const int total = CPS * nb;
+
+    f32x4 acc[T::FM][T::FN];
+    // Subtree values waiting for their right sibling.  Levels below
+    // REG_LEVELS live in registers; with 8 chunks per slice and large wave
+    // tiles the top level (held from chunk 3 to chunk 7) lives in this
+    // wave's own LDS region instead, past the two K-block stages.
+    constexpr int REG_LEVELS = TopLevelInLds<T, CPS>::value ? LOG - 1 : LOG;
+    f32x4 stk[REG_LEVELS > 0 ? REG_LEVELS : 1][T::FM][T::FN];
+    f32x4* lds_top = reinterpret_cast<f32x4*>(smem + 2 * T::STAGE_ELEMS) +
+                     wave * (T::FM * T::FN * 64) + lane;
+    Prefetch<T> pf;
+
+    load_block<T>(pf, g, row0, col0, kslice, kslice + g.Kc, tid);
+    store_block<T>(pf, smem, tid);
+    __syncthreads();
+
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+#pragma unroll
+        for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn)
+                acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        const int cbeg = kslice + c * g.Kc, cend = cbeg + g.Kc;
+        for (int b = 0; b < nb; ++b) {
+            const int t = c * nb + b;
+            const bool more = (t + 1 < total);
+            if (more) {
+                // next block: the following K block of this chunk, or the
+                // first block of the next chunk
+                const int nc = (b + 1 < nb) ? c : c + 1;
+                const int nbi = (b + 1 < nb) ? b + 1 : 0;
+                const int nbeg = kslice + nc * g.Kc;
+                load_block<T>(pf, g, row0, col0, nbeg + nbi * T::BK, nbeg + g.Kc, tid);
+            }
+            const int kb = cbeg + b * T::BK;
+            int nks = (cend - kb + 31) / 32;
+            nks = nks > T::KSTEPS ? T::KSTEPS : nks;
+            const uint16_t* stage = smem + (t & 1) * T::STAGE_ELEMS;
+            if (full)
+                mma_block<T, true>(acc, stage, nks, wm, wn, lane, fm_act, fn_act);
+            else if (fm_act > 0 && fn_act > 0)
+                mma_block<T, false>(acc, stage, nks, wm, wn, lane, fm_act, fn_act);
+            if (more)
+                store_block<T>(pf, smem + ((t + 1) & 1) * T::STAGE_ELEMS, tid);
+            __syncthreads();
+        }
+
+        // fold chunk c into the subtree: one level up per trailing one bit
+#pragma unroll
+        for (int L = 0; L < LOG; ++L) {
+            const bool in_lds = (L >= REG_LEVELS);
+            if (c & (1 << L)) {
+#pragma unroll
+                for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < T::FN; ++fn) {
+                        const f32x4 left = in_lds ? lds_top[(fm * T::FN + fn) * 64]
+                                                  : stk[in_lds ? 0 : L][fm][fn];
+                        acc[fm][fn] = left + acc[fm][fn];
+                    }
+            } else {
+#pragma unroll
+                for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < T::FN; ++fn) {
+                        if (in_lds)
+                            lds_top[(fm * T::FN + fn) * 64] = acc[fm][fn];
+                        else
+                            stk[in_lds ? 0 : L][fm][fn] = acc[fm][fn];
+                    }
+                break;
+            }
+        }
+    }
+    // acc now holds the root of this slice's subtree.
+
+    if (EPI == EPI_STORE) {
+        store_tile<T>(acc, g.Y + (size_t)z * g.out_z_stride, g.ldy, g.M, g.N, wrow0, wcol0,
+                      lane, false);
+        return;
+    }
+    if (EPI == EPI_ATOMIC) {
+        store_tile<T>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
+        return;
+    }
+
+    // EPI_COMBINE: publish the partial, count arrivals, and let the last
+    // slice of this tile add the partials in the fixed tree order.
+    const size_t plane = (size_t)g.M * g.N;
+    store_tile<T>(acc, g.part + (size_t)z * plane, g.N, g.M, g.N, wrow0, wcol0, lane, false);
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        const unsigned prev = __hip_atomic_fetch_add(g.counters + tl, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (unsigned)(8 / CPS - 1));
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __threadfence();
+
+    // a combine only exists when K has 8 chunks, so S = 8 / CPS
+    constexpr int S = 8 / CPS;
+    constexpr int VEC = T::BM * T::BN / 4;
+    for (int v = tid; v < VEC; v += T::THREADS) {
+        const int r = v / (T::BN / 4), cc = 4 * (v % (T::BN / 4));
+        const int row = row0 + r, col = col0 + cc;
+        if (row >= g.M || col >= g.N)
+            continue;
+        const float* p = g.part + (size_t)row * g.N + col;
+        float4 vals[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            vals[s] = *reinterpret_cast<const float4*>(p + (size_t)s * plane);
+        // top levels of the tree over the S slice roots, adjacent pairs
+#pragma unroll
+        for (int w = S; w > 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < (w >> 1); ++i) {
+                vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
+                vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
+                vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
+                vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
+            }
+        *reinterpret_cast<float4*>(g.Y + (size_t)row * g.ldy + col) = vals[0];
+    }
+    if (tid == 0)
+        g.counters[tl] = 0u;  // leave the counter ready for the next call
+}
+
+// Y[e] = fixed tree over count arrays (count in {1,2,4,8}); 4 elements per
+// thread, grid-stride.
+template <int COUNT>
+__global__ __launch_bounds__(256) void tree_combine_kernel(const float* __restrict__ parts,
+                                                           size_t stride,
+                                                           float* __restrict__ Y, size_t n4)
+{
+    for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < n4;
+         v += (size_t)gridDim.x * blockDim.x) {
+        float4 vals[COUNT];
+#pragma unroll
+        for (int s = 0; s < COUNT; ++s)
+            vals[s] = reinterpret_cast<const float4*>(parts + (size_t)s * stride)[v];
+#pragma unroll
+        for (int w = COUNT; w > 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < (w >> 1); ++i) {
+                vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
+                vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
+                vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
+                vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
+            }
+        reinterpret_cast<float4*>(Y)[v] = vals[0];
+    }
+}
+
+// Y[r][0..N) = +0 for r < M (row stride ld); N % 4 == 0.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* Y, long ld, int M, int N)
+{
+    const size_t per_row = (size_t)N / 4;
+    const size_t total = per_row * (size_t)M;
+    for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+         v += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = v / per_row, c = 4 * (v % per_row);
+        *reinterpret_cast<float4*>(Y + r * ld + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// binary32 -> bf16, nearest even; NaN -> quiet NaN of the same sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ x,
+                                                        uint16_t* __restrict__ y, size_t n8)
+{
+    for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < n8;
+         v += (size_t)gridDim.x * blockDim.x) {
+        const float4 a = reinterpret_cast<const float4*>(x)[2 * v];
+        const float4 b = reinterpret_cast<const float4*>(x)[2 * v + 1];
+        uint4 o;
+        o.x = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
+        o.y = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
+        o.z = f32_to_bf16_bits(b.x) | (f32_to_bf16_bits(b.y) << 16);
+        o.w = f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16);
+        reinterpret_cast<uint4*>(y)[v] = o;
+    }
+}
+
+// ---------------------------------------------------------------- launches
+
+template <class T, int CPS, int EPI>
+static hipError_t launch_t(const GemmArgs& g, hipStream_t s)
+{
+    auto fn = slice_gemm_kernel<T, CPS, EPI>;
+    constexpr int lds = lds_bytes<T, CPS>();
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess)
+        return attr;
+    const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(T::THREADS), lds, s, g);
+    return hipGetLastError();
+}
+
+template <class T, int EPI>
+static hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
+{
+    switch (cps) {
+    case 1: return launch_t<T, 1, EPI>(g, s);
+    case 2: return launch_t<T, 2, EPI>(g, s);
+    case 4: return launch_t<T, 4, EPI>(g, s);
+    case 8:
+        if constexpr (EPI == EPI_COMBINE)  // a single slice never needs a combine
+            return hipErrorInvalidValue;
+        else
+            return launch_t<T, 8, EPI>(g, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int EPI>
+static hipError_t launch_tile(int tile, const GemmArgs& g, int cps, hipStream_t s)
+{
+    switch (tile) {
+    case TILE_S16: return launch_cps<TileS16, EPI>(g, cps, s);
+    case TILE_M64: return launch_cps<TileM64, EPI>(g, cps, s);
+    case TILE_L128: return launch_cps<TileL128, EPI>(g, cps, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+void tile_shape(int tile, int* bm, int* bn)
+{
+    switch (tile) {
+    case TILE_S16: *bm = TileS16::BM; *bn = TileS16::BN; return;
+    case TILE_M64: *bm = TileM64::BM; *bn = TileM64::BN; return;
+    default: *bm = TileL128::BM; *bn = TileL128::BN; return;
+    }
+}
+
+hipError_t launch_slice_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s)
+{
+    switch (epi) {
+    case EPI_STORE: return launch_tile<EPI_STORE>(tile, g, cps, s);
+    case EPI_COMBINE: return launch_tile<EPI_COMBINE>(tile, g, cps, s);
+    case EPI_ATOMIC: return launch_tile<EPI_ATOMIC>(tile, g, cps, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+static unsigned grid_for(size_t work, unsigned block)
+{
+    size_t g = (work + block - 1) / block;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+hipError_t launch_tree_combine(const float* parts, size_t stride, int count, float* Y, size_t n,
+                               hipStream_t s)
+{
+    const size_t n4 = n / 4;
+    const dim3 grid(grid_for(n4, 256)), block(256);
+    switch (count) {
+    case 1: hipLaunchKernelGGL(tree_combine_kernel<1>, grid, block, 0, s, parts, stride, Y, n4); break;
+    case 2: hipLaunchKernelGGL(tree_combine_kernel<2>, grid, block, 0, s, parts, stride, Y, n4); break;
+    case 4: hipLaunchKernelGGL(tree_combine_kernel<4>, grid, block, 0, s, parts, stride, Y, n4); break;
+    case 8: hipLaunchKernelGGL(tree_combine_kernel<8>, grid, block, 0, s, parts, stride, Y, n4); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* Y, long ld, int M, int N, hipStream_t s)
+{
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((size_t)M * (N / 4), 256)), dim3(256), 0,
+                       s, Y, ld, M, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* x, uint16_t* y, size_t n, hipStream_t s)
+{
+    const size_t n8 = n / 8;
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, s, x, y, n8);
+    return hipGetLastError();
+}
+
+}  // namespace detred

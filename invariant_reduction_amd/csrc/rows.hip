@@ -1,0 +1,209 @@
+// Batch-invariant row reductions for gfx950: RMSNorm, log_softmax, mean.
+//
+// One workgroup owns one row ("Restoring AI Reproducibility: Thinking
+// Machines Lab's Challenge to Overcome Nondeterminism", 3-1: each batch
+// element handled by one core and reduced in one consistent order).  The
+// order of every reduction depends only on the row length:
+//   1. thread t visits the 16-byte vectors t, t+NT, t+2NT, ... of the row in
+//      that order and the elements of each vector left to right, keeping
+//      one running binary32 value;
+//   2. the 64 lanes of a wave are combined by a butterfly (xor 32,16,..,1);
+//      addition is commutative, so every lane ends with the same bits;
+//   3. the per-wave values are combined through LDS by a fixed butterfly.
+// The batch size, the row's position and the launch never enter.
+//
+// Operations: RMSNorm (the article, 2-3); log_softmax and mean ("Batch
+// Invariant Ops" project summary, Highlighted Details).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace detred {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = v + __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum of one value per wave, identical on every thread of the block.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0)
+        red[wave] = v;
+    __syncthreads();
+    float t = (lane < NW) ? red[lane] : 0.0f;
+#pragma unroll
+    for (int off = NW / 2; off > 0; off >>= 1)
+        t = t + __shfl_xor(t, off, 64);
+    const float total = __shfl(t, 0, 64);
+    __syncthreads();
+    return total;
+}
+
+// ------------------------------------------------------------------ RMSNorm
+constexpr int RMS_THREADS = 256;
+
+__global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ gamma,
+                                                              float* __restrict__ y, int hidden,
+                                                              float eps)
+{
+    __shared__ float red[RMS_THREADS / 64];
+    const size_t row = blockIdx.x;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * hidden);
+    const int nv = hidden / 8;
+
+    float ss = 0.0f;
+    for (int v = threadIdx.x; v < nv; v += RMS_THREADS) {
+        const uint4 q = xr[v];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+            ss = ss + a * a;
+            ss = ss + b * b;
+        }
+    }
+    ss = block_sum<RMS_THREADS / 64>(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
+
+    const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+    float4* yr = reinterpret_cast<float4*>(y + row * hidden);
+    for (int v = threadIdx.x; v < nv; v += RMS_THREADS) {
+        const uint4 q = xr[v], gq = gr[v];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w};
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = (bf16_lo(w[i]) * inv) * bf16_lo(gw[i]);
+            o[2 * i + 1] = (bf16_hi(w[i]) * inv) * bf16_hi(gw[i]);
+        }
+        yr[2 * v] = make_float4(o[0], o[1], o[2], o[3]);
+        yr[2 * v + 1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+// -------------------------------------------------------------- log_softmax
+constexpr int ROW_THREADS = 1024;
+
+// (m, s) stands for s * exp(m): a running maximum and the sum of exp(x - m)
+// of the elements seen.  Merging is commutative bit for bit: the operand
+// with the larger maximum is the one rescaled by 1, and for equal maxima
+// the two sums are added.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2)
+{
+    if (m > m2) {
+        s = s + s2 * expf(m2 - m);
+    } else if (m2 > m) {
+        s = s2 + s * expf(m - m2);
+        m = m2;
+    } else {
+        s = s + s2;
+    }
+}
+
+__global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x, float* y,
+                                                                  int cols)
+{
+    __shared__ float red_m[ROW_THREADS / 64], red_s[ROW_THREADS / 64];
+    const size_t row = blockIdx.x;
+    const float4* xr = reinterpret_cast<const float4*>(x + row * cols);
+    const int nv = cols / 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    float m = -INFINITY, s = 0.0f;
+    for (int v = threadIdx.x; v < nv; v += ROW_THREADS) {
+        const float4 q = xr[v];
+        const float mx = fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w));
+        if (mx > m) {
+            s = s * expf(m - mx);
+            m = mx;
+        }
+        s = s + expf(q.x - m);
+        s = s + expf(q.y - m);
+        s = s + expf(q.z - m);
+        s = s + expf(q.w - m);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
+        lse_merge(m, s, m2, s2);
+    }
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_s[wave] = s;
+    }
+    __syncthreads();
+    constexpr int NW = ROW_THREADS / 64;
+    m = (lane < NW) ? red_m[lane] : -INFINITY;
+    s = (lane < NW) ? red_s[lane] : 0.0f;
+#pragma unroll
+    for (int off = NW / 2; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
+        lse_merge(m, s, m2, s2);
+    }
+    m = __shfl(m, 0, 64);
+    s = __shfl(s, 0, 64);
+    const float ls = logf(s);
+
+    float4* yr = reinterpret_cast<float4*>(y + row * cols);
+    for (int v = threadIdx.x; v < nv; v += ROW_THREADS) {
+        const float4 q = xr[v];
+        yr[v] = make_float4((q.x - m) - ls, (q.y - m) - ls, (q.z - m) - ls, (q.w - m) - ls);
+    }
+}
+
+// --------------------------------------------------------------------- mean
+__global__ __launch_bounds__(ROW_THREADS) void mean_kernel(const float* __restrict__ x,
+                                                           float* __restrict__ y, int cols)
+{
+    __shared__ float red[ROW_THREADS / 64];
+    const size_t row = blockIdx.x;
+    const float4* xr = reinterpret_cast<const float4*>(x + row * cols);
+    const int nv = cols / 4;
+    float s = 0.0f;
+    for (int v = threadIdx.x; v < nv; v += ROW_THREADS) {
+        const float4 q = xr[v];
+        s = s + q.x;
+        s = s + q.y;
+        s = s + q.z;
+        s = s + q.w;
+    }
+    s = block_sum<ROW_THREADS / 64>(s, red);
+    if (threadIdx.x == 0)
+        y[row] = s / (float)cols;
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows,
+                          int hidden, float eps, hipStream_t s)
+{
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(RMS_THREADS), 0, s, x, gamma, y, hidden,
+                       eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s)
+{
+    hipLaunchKernelGGL(log_softmax_kernel, dim3(rows), dim3(ROW_THREADS), 0, s, x, y, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_mean(const float* x, float* y, int rows, int cols, hipStream_t s)
+{
+    hipLaunchKernelGGL(mean_kernel, dim3(rows), dim3(ROW_THREADS), 0, s, x, y, cols);
+    return hipGetLastError();
+}
+
+}  // namespace detred

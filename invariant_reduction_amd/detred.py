@@ -1,0 +1,254 @@
+"""ctypes binding of libdetred (include/detred.h).
+
+Argument marshalling only: each function takes torch tensors, checks dtypes
+and devices, and passes raw device pointers, leading dimensions and the
+current HIP stream to the C entry point of the same name.  Every operation
+runs in the library's HIP kernels; there is no fallback.  A non-OK status
+raises DetredError.
+
+bf16 tensors may be given as torch.bfloat16, torch.int16 or torch.uint16
+(the bit patterns are what the library reads).
+"""
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+_F = ctypes.c_float
+
+# name -> argument types, in header order
+SIGNATURES = {
+    "detred_status_string": ([_I], ctypes.c_char_p),
+    "detred_version": ([], _I),
+    "detred_policy": ([_I, _I, _P, _P, _P, _P, _P], _I),
+    "detred_gemm_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "detred_workspace_init": ([_P, _Z, _P], _I),
+    "det_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "atomic_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
+    "tree_tp_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "tree_tp_shard_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
+    "tree_combine_f32": ([_P, _Z, _I, _P, _Z, _P], _I),
+    "detred_f32_to_bf16": ([_P, _P, _Z, _P], _I),
+    "inv_rmsnorm": ([_P, _P, _P, _I, _I, _F, _P], _I),
+    "inv_log_softmax": ([_P, _P, _I, _I, _P], _I),
+    "inv_mean": ([_P, _P, _I, _I, _P], _I),
+}
+
+
+class DetredError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+def lib_path():
+    return _build.LIB
+
+
+def lib():
+    """Load libdetred.so, building it first if it is not there.  Raises if
+    the library cannot be built or loaded: there is no other path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    for name, (args, res) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().detred_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != OK:
+        raise DetredError(status, where)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _mat(t, dtypes, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dim() != 2 or (t.shape[0] > 1 and t.stride(1) != 1) or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be a row-major matrix with unit column stride" % name)
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return ctypes.c_void_p(t.data_ptr()), int(ld)
+
+
+def policy(N, K):
+    """The locked policy for (N, K): dict with chunks, chunk_k, tile_m,
+    tile_n, default_split."""
+    vals = [ctypes.c_int() for _ in range(5)]
+    _check(lib().detred_policy(N, K, *[ctypes.byref(v) for v in vals]), "detred_policy")
+    keys = ["chunks", "chunk_k", "tile_m", "tile_n", "default_split"]
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+detred_policy = policy
+
+
+def detred_gemm_workspace_bytes(M, N, K, split_or_shards):
+    return int(lib().detred_gemm_workspace_bytes(M, N, K, split_or_shards))
+
+
+def detred_workspace_init(ws, stream=None):
+    _check(lib().detred_workspace_init(ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "detred_workspace_init")
+
+
+def workspace(M, N, K, split_or_shards, device="cuda", stream=None):
+    """Allocate (through torch) and zero a workspace for an M x N x K
+    product with the given split or shard count; None when none is needed."""
+    nbytes = detred_gemm_workspace_bytes(M, N, K, split_or_shards)
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
+    detred_workspace_init(ws, stream)
+    return ws
+
+
+def _ws(ws):
+    if ws is None:
+        return ctypes.c_void_p(None), 0
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def _gemm_dims(X, W, Y):
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K or tuple(Y.shape) != (M, N):
+        raise ValueError("shape mismatch: X %s, W %s, Y %s" % (tuple(X.shape), tuple(W.shape), tuple(Y.shape)))
+    return M, N, K
+
+
+def det_splitk_gemm(X, W, Y, split_k=0, ws=None, stream=None):
+    """Y[M,N] (fp32) = X[M,K] W[K,N] (bf16) with the fixed chunk tree."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    py, ldy = _mat(Y, (torch.float32,), "Y")
+    M, N, K = _gemm_dims(X, W, Y)
+    pws, nws = _ws(ws)
+    _check(lib().det_splitk_gemm(px, ldx, pw, ldw, py, ldy, M, N, K, split_k, pws, nws,
+                                 _stream(stream)), "det_splitk_gemm")
+
+
+def atomic_splitk_gemm(X, W, Y, split_k=0, stream=None):
+    """The nondeterministic control: zero Y, then fp32 atomic slice adds."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    py, ldy = _mat(Y, (torch.float32,), "Y")
+    M, N, K = _gemm_dims(X, W, Y)
+    _check(lib().atomic_splitk_gemm(px, ldx, pw, ldw, py, ldy, M, N, K, split_k,
+                                    _stream(stream)), "atomic_splitk_gemm")
+
+
+def tree_tp_gemm(X, W, Y, tp_shards, ws=None, stream=None):
+    """Tree-based TP-invariant product over tp_shards virtual shards."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    py, ldy = _mat(Y, (torch.float32,), "Y")
+    M, N, K = _gemm_dims(X, W, Y)
+    pws, nws = _ws(ws)
+    _check(lib().tree_tp_gemm(px, ldx, pw, ldw, py, ldy, M, N, K, tp_shards, pws, nws,
+                              _stream(stream)), "tree_tp_gemm")
+
+
+def tree_tp_shard_gemm(Xt, Wt, Pt, tp_shards, stream=None):
+    """One rank's shard of tree_tp_gemm: Pt = subtree root of Xt Wt."""
+    px, ldx = _mat(Xt, _BF16_TYPES, "Xt")
+    pw, ldw = _mat(Wt, _BF16_TYPES, "Wt")
+    pp, ldp = _mat(Pt, (torch.float32,), "Pt")
+    M, N, Kt = _gemm_dims(Xt, Wt, Pt)
+    _check(lib().tree_tp_shard_gemm(px, ldx, pw, ldw, pp, ldp, M, N, Kt, tp_shards,
+                                    _stream(stream)), "tree_tp_shard_gemm")
+
+
+def tree_combine_f32(parts, Y, stream=None):
+    """Y = fixed binary tree over parts[0..count) (parts: [count, ...] fp32,
+    contiguous; Y: contiguous fp32 with parts[0]'s element count)."""
+    if parts.dtype != torch.float32 or Y.dtype != torch.float32 or not parts.is_cuda or not Y.is_cuda:
+        raise TypeError("parts and Y must be fp32 GPU tensors")
+    if not parts.is_contiguous() or not Y.is_contiguous():
+        raise ValueError("parts and Y must be contiguous")
+    count = parts.shape[0]
+    n = parts[0].numel()
+    if Y.numel() != n:
+        raise ValueError("Y must have %d elements" % n)
+    _check(lib().tree_combine_f32(ctypes.c_void_p(parts.data_ptr()), n, count,
+                                  ctypes.c_void_p(Y.data_ptr()), n, _stream(stream)),
+           "tree_combine_f32")
+
+
+def detred_f32_to_bf16(x, y, stream=None):
+    """y (bf16 bits) = nearest-even bf16 of x (fp32); both contiguous."""
+    if x.dtype != torch.float32 or y.dtype not in _BF16_TYPES or not x.is_cuda or not y.is_cuda:
+        raise TypeError("x must be fp32 and y bf16/int16 GPU tensors")
+    if not x.is_contiguous() or not y.is_contiguous() or x.numel() != y.numel():
+        raise ValueError("x and y must be contiguous with equal element counts")
+    _check(lib().detred_f32_to_bf16(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                    x.numel(), _stream(stream)), "detred_f32_to_bf16")
+
+
+def _rows(t, dtypes, name):
+    if t.dtype not in dtypes or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+        raise TypeError("%s must be a contiguous 2-D GPU tensor of %s" % (name, dtypes))
+    return ctypes.c_void_p(t.data_ptr()), t.shape[0], t.shape[1]
+
+
+def inv_rmsnorm(x, gamma, y, eps, stream=None):
+    """y[rows,hidden] fp32 = RMSNorm(x bf16) * gamma (bf16)."""
+    px, rows, hidden = _rows(x, _BF16_TYPES, "x")
+    py, r2, h2 = _rows(y, (torch.float32,), "y")
+    if gamma.dtype not in _BF16_TYPES or not gamma.is_cuda or not gamma.is_contiguous() or gamma.numel() != hidden:
+        raise TypeError("gamma must be a contiguous bf16 GPU vector of length hidden")
+    if (r2, h2) != (rows, hidden):
+        raise ValueError("y must match x's shape")
+    _check(lib().inv_rmsnorm(px, ctypes.c_void_p(gamma.data_ptr()), py, rows, hidden,
+                             float(eps), _stream(stream)), "inv_rmsnorm")
+
+
+def inv_log_softmax(x, y, stream=None):
+    """y = log_softmax(x) over the last dim (fp32)."""
+    px, rows, cols = _rows(x, (torch.float32,), "x")
+    py, r2, c2 = _rows(y, (torch.float32,), "y")
+    if (r2, c2) != (rows, cols):
+        raise ValueError("y must match x's shape")
+    _check(lib().inv_log_softmax(px, py, rows, cols, _stream(stream)), "inv_log_softmax")
+
+
+def inv_mean(x, y, stream=None):
+    """y[rows] = mean of x over the last dim (fp32)."""
+    px, rows, cols = _rows(x, (torch.float32,), "x")
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.numel() != rows:
+        raise TypeError("y must be a contiguous fp32 GPU vector with one element per row")
+    _check(lib().inv_mean(px, ctypes.c_void_p(y.data_ptr()), rows, cols, _stream(stream)),
+           "inv_mean")

@@ -1,0 +1,128 @@
+"""The C-ABI library: it loads, exports every entry point include/detred.h
+declares, and rejects bad arguments before any GPU work.  CPU only: no
+call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from invariant_reduction_amd import detred
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "detred.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for must in ["det_splitk_gemm", "atomic_splitk_gemm", "tree_tp_gemm", "inv_rmsnorm",
+                 "inv_log_softmax", "inv_mean"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = detred.lib()
+    missing = [n for n in header_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(header_functions()) == set(detred.SIGNATURES), \
+        "binding signatures out of sync with the header"
+
+
+def test_status_strings_and_version():
+    assert detred.status_string(0) == "DETRED_OK"
+    for s in range(1, 5):
+        assert detred.status_string(s).startswith("DETRED_E")
+    assert detred.lib().detred_version() >= 100
+
+
+def test_policy_is_locked_by_n_and_k():
+    p = detred.policy(16, 512)
+    assert p["chunks"] == 8 and p["chunk_k"] == 64 and p["default_split"] == 8
+    p = detred.policy(14336, 4096)
+    assert p["chunks"] == 8 and p["chunk_k"] == 512 and p["default_split"] == 1
+    assert (p["tile_m"], p["tile_n"]) == (128, 128)
+    p = detred.policy(4096, 64)  # LoRA expand: K = r < 256 -> one chunk
+    assert p["chunks"] == 1 and p["chunk_k"] == 64 and p["default_split"] == 1
+    p = detred.policy(64, 264)   # K not a multiple of 256 -> one chunk
+    assert p["chunks"] == 1
+    assert detred.lib().detred_policy(-1, 4, None, None, None, None, None) == detred.EINVAL
+
+
+def test_workspace_bytes():
+    assert detred.detred_gemm_workspace_bytes(16, 16, 512, 1) == 0
+    n = detred.detred_gemm_workspace_bytes(16, 16, 512, 8)
+    assert n >= 8 * 16 * 16 * 4 + 4 and n % 256 == 0
+    assert detred.detred_gemm_workspace_bytes(16, 16, 512, 3) == 0
+
+
+A16 = 0x10000          # fake, 16-byte aligned addresses: never dereferenced
+A16b = 0x20000
+A16c = 0x30000
+MIS = 0x10002          # misaligned
+
+
+def call_det(X=A16, ldx=512, W=A16b, ldw=16, Y=A16c, ldy=16, M=16, N=16, K=512, S=8,
+             ws=None, nws=0):
+    return detred.lib().det_splitk_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, S, ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), detred.EINVAL),
+    (dict(K=-8), detred.EINVAL),
+    (dict(ldx=100), detred.EINVAL),              # ldx < K
+    (dict(ldw=8), detred.EINVAL),                # ldw < N
+    (dict(ldy=8), detred.EINVAL),                # ldy < N
+    (dict(X=None), detred.EINVAL),
+    (dict(W=None), detred.EINVAL),
+    (dict(Y=None), detred.EINVAL),
+    (dict(X=MIS), detred.EINVAL),
+    (dict(Y=MIS), detred.EINVAL),
+    (dict(ldx=516), detred.EINVAL),              # row stride not 16-byte aligned
+    (dict(K=500, ldx=504), detred.EUNSUPPORTED),  # K % 8 != 0
+    (dict(N=12, ldw=16, ldy=16), detred.EUNSUPPORTED),  # N % 8 != 0
+    (dict(S=3), detred.EUNSUPPORTED),
+    (dict(S=16), detred.EUNSUPPORTED),
+    (dict(K=264, ldx=264, S=2), detred.EUNSUPPORTED),  # one chunk only
+    (dict(S=8, ws=None), detred.EWORKSPACE),
+    (dict(S=8, ws=0x100000, nws=64), detred.EWORKSPACE),
+    (dict(S=8, ws=0x100010, nws=1 << 20), detred.EWORKSPACE),  # not 256-aligned
+])
+def test_det_splitk_rejects(kw, status):
+    assert call_det(**kw) == status
+
+
+def test_empty_problem_launches_nothing():
+    # M == 0 or N == 0: OK without touching the (null) pointers
+    assert call_det(X=None, W=None, Y=None, M=0) == detred.OK
+    assert detred.lib().atomic_splitk_gemm(None, 512, None, 0, None, 0, 16, 0, 512, 8, None) == detred.OK
+    assert detred.lib().tree_tp_gemm(None, 8, None, 8, None, 8, 0, 8, 8, 1, None, 0, None) == detred.OK
+
+
+def test_other_entry_points_reject():
+    L = detred.lib()
+    assert L.atomic_splitk_gemm(A16, 512, A16b, 16, A16c, 16, 16, 16, 512, 5, None) == detred.EUNSUPPORTED
+    assert L.tree_tp_gemm(A16, 512, A16b, 16, A16c, 16, 16, 16, 512, 3, None, 0, None) == detred.EUNSUPPORTED
+    assert L.tree_tp_gemm(A16, 512, A16b, 16, A16c, 16, 16, 16, 512, 4, None, 0, None) == detred.EWORKSPACE
+    assert L.tree_tp_shard_gemm(A16, 64, A16b, 16, A16c, 16, 16, 16, 64, 6, None) == detred.EINVAL
+    assert L.tree_tp_shard_gemm(A16, 40, A16b, 16, A16c, 16, 16, 16, 40, 2, None) == detred.EUNSUPPORTED
+    assert L.tree_combine_f32(A16, 16, 3, A16b, 16, None) == detred.EUNSUPPORTED
+    assert L.tree_combine_f32(A16, 8, 2, A16b, 16, None) == detred.EINVAL   # stride < n
+    assert L.tree_combine_f32(MIS, 16, 2, A16b, 16, None) == detred.EINVAL
+    assert L.detred_f32_to_bf16(A16, A16b, 12, None) == detred.EUNSUPPORTED
+    assert L.detred_f32_to_bf16(None, A16b, 16, None) == detred.EINVAL
+    assert L.inv_rmsnorm(A16, A16b, A16c, 4, 4100, ctypes.c_float(1e-6), None) == detred.EUNSUPPORTED
+    assert L.inv_rmsnorm(A16, None, A16c, 4, 4096, ctypes.c_float(1e-6), None) == detred.EINVAL
+    assert L.inv_rmsnorm(A16, A16b, A16c, -1, 4096, ctypes.c_float(1e-6), None) == detred.EINVAL
+    assert L.inv_rmsnorm(None, None, None, 0, 4096, ctypes.c_float(1e-6), None) == detred.OK
+    assert L.inv_log_softmax(A16, A16b, 4, 6, None) == detred.EUNSUPPORTED
+    assert L.inv_log_softmax(MIS, A16b, 4, 8, None) == detred.EINVAL
+    assert L.inv_mean(A16, A16b, 4, 0, None) == detred.EUNSUPPORTED
+    assert L.inv_mean(None, A16b, 4, 8, None) == detred.EINVAL
+    assert L.detred_workspace_init(None, 16, None) == detred.EINVAL

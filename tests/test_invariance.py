@@ -1,0 +1,147 @@
+"""Bit-level invariance on the GPU: a row's output does not depend on the
+batch size M, on the row's position in the batch, on the split count, on
+the virtual tensor-parallel shard count, or on replay.  The atomic control's
+replay divergence is measured and printed, not asserted."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_bitwise, bits, dev_bf16, host
+from invariant_reduction_amd import detred, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def det(Xd, Wd, S, dev, M=None):
+    M = Xd.shape[0] if M is None else M
+    N, K = Wd.shape[1], Wd.shape[0]
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = detred.workspace(M, N, K, S if S else detred.policy(N, K)["default_split"], dev)
+    detred.det_splitk_gemm(Xd[:M], Wd, Y, S, ws)
+    return Y
+
+
+def test_shrink_16x512x16_batch1_equals_batch16(dev):
+    """Row 0 computed alone (M=1) equals row 0 of the M=16 batch, for the
+    deterministic split-K=8 tree and the unsplit reduction."""
+    X, A, _ = inputs.lora_inputs(16, 512, 16, seed=0)
+    Xd, Ad = dev_bf16(X, dev), dev_bf16(A, dev)
+    for S in (8, 1):
+        y16 = det(Xd, Ad, S, dev)
+        y1 = det(Xd, Ad, S, dev, M=1)
+        torch.cuda.synchronize()
+        assert_bitwise(y1[0], y16[0], "row 0 at M=1 vs M=16, S=%d" % S)
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_shrink_every_m_1_to_4096(r, dev):
+    """LoRA shrink X[M,4096] A[4096,r]: for every M in 1..4096 the rows equal
+    the M=4096 rows bit for bit (default split, 8 slices)."""
+    X, A, _ = inputs.lora_inputs(4096, 4096, r, seed=0)
+    Xd, Ad = dev_bf16(X, dev), dev_bf16(A, dev)
+    ref = det(Xd, Ad, 0, dev)
+    ws = detred.workspace(4096, r, 4096, 8, dev)
+    out = torch.empty((4096, r), dtype=torch.float32, device=dev)
+    bad = []
+    for M in range(1, 4097):
+        detred.det_splitk_gemm(Xd[:M], Ad, out[:M], 0, ws)
+        if not torch.equal(out[:M].view(torch.int32), ref[:M].view(torch.int32)):
+            bad.append(M)
+            if len(bad) > 5:
+                break
+    assert not bad, "rows differ for M in %s" % bad
+
+
+DENSE_M = [1, 2, 3, 15, 16, 17, 31, 33, 127, 128, 129, 1000, 1023, 1024, 1025, 4095, 4096]
+
+
+def test_dense_rows_invariant_across_m(dev):
+    X, W = inputs.dense_inputs(4096, 4096, 14336, seed=0)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    ref = det(Xd, Wd, 0, dev)
+    Y = torch.empty_like(ref)
+    for M in DENSE_M:
+        detred.det_splitk_gemm(Xd[:M], Wd, Y[:M], 0, None)
+        torch.cuda.synchronize()
+        assert torch.equal(Y[:M].view(torch.int32), ref[:M].view(torch.int32)), "M=%d" % M
+
+
+def test_position_invariance(dev):
+    """f(X[j:j+1])[0] == f(X)[j], and permuting the rows permutes the output."""
+    cases = [(256, 64, 4096), (300, 16, 512), (257, 264, 2048)]
+    for (M, N, K) in cases:
+        X, W = inputs.dense_inputs(M, K, N, seed=2)
+        Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+        ref = det(Xd, Wd, 0, dev)
+        for j in (0, 1, 17, 63, 64, M - 1):
+            yj = det(Xd[j:j + 1].contiguous(), Wd, 0, dev)
+            torch.cuda.synchronize()
+            assert_bitwise(yj[0], ref[j], "row %d alone, shape %s" % (j, (M, N, K)))
+        perm = torch.from_numpy(np.random.default_rng(M).permutation(M)).to(dev)
+        yp = det(Xd[perm].contiguous(), Wd, 0, dev)
+        torch.cuda.synchronize()
+        assert_bitwise(yp, ref[perm], "permuted rows, shape %s" % ((M, N, K),))
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 512), (256, 64, 4096), (128, 14336, 4096),
+                                   (512, 8192, 8192)])
+def test_split_and_tp_invariance(M, N, K, dev):
+    """det S in {1,2,4,8} and tree_tp T in {1,2,4,8} give one bit pattern;
+    so does every shard run at its own share shape plus the tree combine."""
+    X, W = inputs.dense_inputs(M, K, N, seed=5)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    ref = det(Xd, Wd, 1, dev)
+    for S in (2, 4, 8):
+        assert_bitwise(det(Xd, Wd, S, dev), ref, "det S=%d" % S)
+    for T in (1, 2, 4, 8):
+        Y = torch.empty_like(ref)
+        ws = detred.workspace(M, N, K, T, dev)
+        detred.tree_tp_gemm(Xd, Wd, Y, T, ws)
+        torch.cuda.synchronize()
+        assert_bitwise(Y, ref, "tree_tp T=%d" % T)
+        del ws
+        # each rank's share: X[:, Kt-slice] (copied, as a rank would hold it)
+        Kt = K // T
+        parts = torch.empty((T, M, N), dtype=torch.float32, device=dev)
+        for t in range(T):
+            Xt = Xd[:, t * Kt:(t + 1) * Kt].contiguous()
+            Wt = Wd[t * Kt:(t + 1) * Kt].contiguous()
+            detred.tree_tp_shard_gemm(Xt, Wt, parts[t], T)
+        Yc = torch.empty_like(ref)
+        detred.tree_combine_f32(parts, Yc)
+        torch.cuda.synchronize()
+        assert_bitwise(Yc, ref, "shards at share shape + combine, T=%d" % T)
+
+
+def _digest(t):
+    return hashlib.sha1(host(t).tobytes()).hexdigest()
+
+
+def test_replays_det_identical_atomic_reported(dev):
+    """100 identical-input replays: the deterministic tree gives one output;
+    the atomic control's divergence is printed (share of replays 1..99 that
+    differ from replay 0, unique outputs, mean share of differing elements)."""
+    X, A, _ = inputs.lora_inputs(16, 512, 16, seed=0)
+    Xd, Ad = dev_bf16(X, dev), dev_bf16(A, dev)
+    for (M, r, K) in [(16, 16, 512), (256, 64, 4096)]:
+        if K != 512:
+            X, A, _ = inputs.lora_inputs(M, K, r, seed=0)
+            Xd, Ad = dev_bf16(X, dev), dev_bf16(A, dev)
+        ws = detred.workspace(M, r, K, 8, dev)
+        Y = torch.empty((M, r), dtype=torch.float32, device=dev)
+        det_hashes, atom = set(), []
+        for _ in range(100):
+            detred.det_splitk_gemm(Xd, Ad, Y, 8, ws)
+            det_hashes.add(_digest(Y))
+        for _ in range(100):
+            detred.atomic_splitk_gemm(Xd, Ad, Y, 8)
+            atom.append(bits(Y).copy())
+        assert len(det_hashes) == 1, "det split-K=8 replays gave %d outputs" % len(det_hashes)
+        differ = [not np.array_equal(a, atom[0]) for a in atom[1:]]
+        frac = np.mean([np.mean(a != atom[0]) for a in atom[1:]])
+        uniq = len({a.tobytes() for a in atom})
+        print("\natomic split-K=8 %dx%dx%d: %.2f%% of replays differ from replay 0, "
+              "%d unique outputs of 100, %.3f%% of elements differ on average"
+              % (M, r, K, 100.0 * np.mean(differ), uniq, 100.0 * frac))

@@ -1,0 +1,130 @@
+"""GPU parity and invariance of the row reductions (RMSNorm, log_softmax,
+mean) against the fp64 oracle.  Tolerances scale with the magnitudes that
+combine into each element:
+  RMSNorm     |d| <= 1e-5 * |y| + 1e-6
+  log_softmax |d| <= 1e-5 * (|x - m| + |ln s|) + 1e-6
+  mean        |d| <= 1e-5 * sum|x| / V + 1e-6"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_bitwise, dev_bf16, dev_f32, host
+from invariant_reduction_amd import detred, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_rms(x, g, eps, dev):
+    y = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    detred.inv_rmsnorm(dev_bf16(x, dev), dev_bf16(g, dev), y, eps)
+    return y
+
+
+@pytest.mark.parametrize("B,H", [(1, 4096), (16, 4096), (256, 4096), (4096, 4096),
+                                 (3, 8), (5, 2056), (7, 12288), (2, 65536)])
+def test_rmsnorm_parity(B, H, dev):
+    x, g = inputs.rmsnorm_inputs(B, H, seed=B + H)
+    y = host(gpu_rms(x, g, 1e-6, dev)).astype(np.float64)
+    rows = slice(None) if B <= 256 else np.arange(0, B, 37)
+    ref = oracle.rmsnorm(x[rows], g, 1e-6)
+    assert np.all(np.abs(y[rows] - ref) <= 1e-5 * np.abs(ref) + 1e-6)
+
+
+def test_rmsnorm_closed_forms(dev):
+    H = 4096
+    rng = np.random.default_rng(2)
+    x = inputs.f32_bits_to_bf16_bits(np.where(rng.random((4, H)) < 0.5, -1.0, 1.0).astype(np.float32))
+    _, g = inputs.rmsnorm_inputs(1, H)
+    y = host(gpu_rms(x, g, 1e-6, dev)).astype(np.float64)
+    want = inputs.bf16_bits_to_f32(g) * inputs.bf16_bits_to_f32(x) * 0.999999500000375
+    assert np.all(np.abs(y - want) <= 1e-5 * np.abs(want) + 1e-6)
+
+
+def test_rmsnorm_batch_invariance(dev):
+    x, g = inputs.rmsnorm_inputs(4096, 4096, seed=0)
+    ref = gpu_rms(x, g, 1e-6, dev)
+    for B in (1, 16, 256, 4095):
+        assert_bitwise(gpu_rms(x[:B], g, 1e-6, dev), ref[:B], "rmsnorm B=%d prefix" % B)
+    for j in (0, 100, 4095):
+        assert_bitwise(gpu_rms(x[j:j + 1], g, 1e-6, dev)[0], ref[j], "rmsnorm row %d alone" % j)
+    for _ in range(5):
+        assert_bitwise(gpu_rms(x, g, 1e-6, dev), ref, "rmsnorm replay")
+
+
+def lsm_tol(x, ref):
+    x = x.astype(np.float64)
+    m = x.max(axis=1, keepdims=True)
+    ls = np.log(np.exp(x - m).sum(axis=1, keepdims=True))
+    return 1e-5 * (np.abs(x - m) + np.abs(ls)) + 1e-6
+
+
+@pytest.mark.parametrize("B,V", [(1, 151936), (16, 151936), (256, 151936), (3, 4),
+                                 (5, 1000), (2, 4100), (9, 65540)])
+def test_log_softmax_parity(B, V, dev):
+    x = inputs.logits_inputs(B, V, seed=B + V)
+    y = torch.empty((B, V), dtype=torch.float32, device=dev)
+    detred.inv_log_softmax(dev_f32(x, dev), y)
+    yh = host(y).astype(np.float64)
+    ref = oracle.log_softmax(x)
+    assert np.all(np.abs(yh - ref) <= lsm_tol(x, ref))
+
+
+def test_log_softmax_in_place_and_constant_row(dev):
+    x = inputs.logits_inputs(4, 151936, seed=7)
+    xd = dev_f32(x, dev)
+    y = torch.empty_like(xd)
+    detred.inv_log_softmax(xd, y)
+    detred.inv_log_softmax(xd, xd)
+    torch.cuda.synchronize()
+    assert_bitwise(xd, y, "in place vs out of place")
+    c = dev_f32(np.full((2, 151936), 1.75, np.float32), dev)
+    detred.inv_log_softmax(c, c)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(c) + 11.931214658529285) <= 1e-5 * 11.93 + 1e-6)
+
+
+@pytest.mark.parametrize("B,V", [(1, 151936), (16, 151936), (256, 151936), (1, 4),
+                                 (7, 1004), (3, 65540)])
+def test_mean_parity(B, V, dev):
+    x = inputs.logits_inputs(B, V, seed=3 * B + V)
+    y = torch.empty(B, dtype=torch.float32, device=dev)
+    detred.inv_mean(dev_f32(x, dev), y)
+    ref = oracle.mean(x)
+    tol = 1e-5 * np.abs(x.astype(np.float64)).sum(axis=1) / V + 1e-6
+    assert np.all(np.abs(host(y).astype(np.float64) - ref) <= tol)
+
+
+def test_mean_integer_rows_exact(dev):
+    V = 151936
+    x = inputs.integer_f32((8, V), -8, 8, 5, 4)
+    y = torch.empty(8, dtype=torch.float32, device=dev)
+    detred.inv_mean(dev_f32(x, dev), y)
+    ref = oracle.mean(x).astype(np.float32)  # exact sum, then one rounding of sum/V
+    np.testing.assert_array_equal(host(y), ref)
+
+
+def test_logit_ops_batch_invariance(dev):
+    V = 151936
+    x = inputs.logits_inputs(300, V, seed=0)
+    xd = dev_f32(x, dev)
+    ref_l = torch.empty_like(xd)
+    detred.inv_log_softmax(xd, ref_l)
+    ref_m = torch.empty(300, dtype=torch.float32, device=dev)
+    detred.inv_mean(xd, ref_m)
+    for B in (1, 16, 256, 299):
+        yl = torch.empty((B, V), dtype=torch.float32, device=dev)
+        detred.inv_log_softmax(xd[:B], yl)
+        ym = torch.empty(B, dtype=torch.float32, device=dev)
+        detred.inv_mean(xd[:B], ym)
+        torch.cuda.synchronize()
+        assert_bitwise(yl, ref_l[:B], "log_softmax B=%d" % B)
+        assert_bitwise(ym, ref_m[:B], "mean B=%d" % B)
+    for j in (0, 123, 299):
+        yl = torch.empty((1, V), dtype=torch.float32, device=dev)
+        detred.inv_log_softmax(xd[j:j + 1], yl)
+        ym = torch.empty(1, dtype=torch.float32, device=dev)
+        detred.inv_mean(xd[j:j + 1], ym)
+        torch.cuda.synchronize()
+        assert_bitwise(yl[0], ref_l[j], "log_softmax row %d alone" % j)
+        assert_bitwise(ym[0], ref_m[j], "mean row %d alone" % j)
