@@ -80,6 +80,32 @@ def _check(status, where):
         raise DetredError(status, where)
 
 
+def _entry(marshal):
+    """Turn a marshaller (torch arguments -> C name and ctypes arguments)
+    into the public call; ``prepare`` keeps the marshalled arguments for
+    repeated launches without re-marshalling."""
+    def call(*args, **kw):
+        name, cargs = marshal(*args, **kw)
+        _check(getattr(lib(), name)(*cargs), name)
+    call.__name__ = marshal.__name__
+    call.__doc__ = marshal.__doc__
+    call.marshal = marshal
+    return call
+
+
+def prepare(fn, *args, **kw):
+    """Marshal once; return a zero-argument callable that issues the same C
+    call (same pointers, sizes and stream) each time it is called."""
+    name, cargs = fn.marshal(*args, **kw)
+    cfun = getattr(lib(), name)
+
+    def launch():
+        st = cfun(*cargs)
+        if st != OK:
+            raise DetredError(st, name)
+    return launch
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -150,6 +176,7 @@ def _gemm_dims(X, W, Y):
     return M, N, K
 
 
+@_entry
 def det_splitk_gemm(X, W, Y, split_k=0, ws=None, stream=None):
     """Y[M,N] (fp32) = X[M,K] W[K,N] (bf16) with the fixed chunk tree."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
@@ -157,20 +184,22 @@ def det_splitk_gemm(X, W, Y, split_k=0, ws=None, stream=None):
     py, ldy = _mat(Y, (torch.float32,), "Y")
     M, N, K = _gemm_dims(X, W, Y)
     pws, nws = _ws(ws)
-    _check(lib().det_splitk_gemm(px, ldx, pw, ldw, py, ldy, M, N, K, split_k, pws, nws,
-                                 _stream(stream)), "det_splitk_gemm")
+    return "det_splitk_gemm", (px, ldx, pw, ldw, py, ldy, M, N, K, split_k, pws, nws,
+                                 _stream(stream))
 
 
+@_entry
 def atomic_splitk_gemm(X, W, Y, split_k=0, stream=None):
     """The nondeterministic control: zero Y, then fp32 atomic slice adds."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
     pw, ldw = _mat(W, _BF16_TYPES, "W")
     py, ldy = _mat(Y, (torch.float32,), "Y")
     M, N, K = _gemm_dims(X, W, Y)
-    _check(lib().atomic_splitk_gemm(px, ldx, pw, ldw, py, ldy, M, N, K, split_k,
-                                    _stream(stream)), "atomic_splitk_gemm")
+    return "atomic_splitk_gemm", (px, ldx, pw, ldw, py, ldy, M, N, K, split_k,
+                                    _stream(stream))
 
 
+@_entry
 def tree_tp_gemm(X, W, Y, tp_shards, ws=None, stream=None):
     """Tree-based TP-invariant product over tp_shards virtual shards."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
@@ -178,20 +207,22 @@ def tree_tp_gemm(X, W, Y, tp_shards, ws=None, stream=None):
     py, ldy = _mat(Y, (torch.float32,), "Y")
     M, N, K = _gemm_dims(X, W, Y)
     pws, nws = _ws(ws)
-    _check(lib().tree_tp_gemm(px, ldx, pw, ldw, py, ldy, M, N, K, tp_shards, pws, nws,
-                              _stream(stream)), "tree_tp_gemm")
+    return "tree_tp_gemm", (px, ldx, pw, ldw, py, ldy, M, N, K, tp_shards, pws, nws,
+                              _stream(stream))
 
 
+@_entry
 def tree_tp_shard_gemm(Xt, Wt, Pt, tp_shards, stream=None):
     """One rank's shard of tree_tp_gemm: Pt = subtree root of Xt Wt."""
     px, ldx = _mat(Xt, _BF16_TYPES, "Xt")
     pw, ldw = _mat(Wt, _BF16_TYPES, "Wt")
     pp, ldp = _mat(Pt, (torch.float32,), "Pt")
     M, N, Kt = _gemm_dims(Xt, Wt, Pt)
-    _check(lib().tree_tp_shard_gemm(px, ldx, pw, ldw, pp, ldp, M, N, Kt, tp_shards,
-                                    _stream(stream)), "tree_tp_shard_gemm")
+    return "tree_tp_shard_gemm", (px, ldx, pw, ldw, pp, ldp, M, N, Kt, tp_shards,
+                                    _stream(stream))
 
 
+@_entry
 def tree_combine_f32(parts, Y, stream=None):
     """Y = fixed binary tree over parts[0..count) (parts: [count, ...] fp32,
     contiguous; Y: contiguous fp32 with parts[0]'s element count)."""
@@ -203,19 +234,19 @@ def tree_combine_f32(parts, Y, stream=None):
     n = parts[0].numel()
     if Y.numel() != n:
         raise ValueError("Y must have %d elements" % n)
-    _check(lib().tree_combine_f32(ctypes.c_void_p(parts.data_ptr()), n, count,
-                                  ctypes.c_void_p(Y.data_ptr()), n, _stream(stream)),
-           "tree_combine_f32")
+    return "tree_combine_f32", (ctypes.c_void_p(parts.data_ptr()), n, count,
+                                  ctypes.c_void_p(Y.data_ptr()), n, _stream(stream))
 
 
+@_entry
 def detred_f32_to_bf16(x, y, stream=None):
     """y (bf16 bits) = nearest-even bf16 of x (fp32); both contiguous."""
     if x.dtype != torch.float32 or y.dtype not in _BF16_TYPES or not x.is_cuda or not y.is_cuda:
         raise TypeError("x must be fp32 and y bf16/int16 GPU tensors")
     if not x.is_contiguous() or not y.is_contiguous() or x.numel() != y.numel():
         raise ValueError("x and y must be contiguous with equal element counts")
-    _check(lib().detred_f32_to_bf16(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
-                                    x.numel(), _stream(stream)), "detred_f32_to_bf16")
+    return "detred_f32_to_bf16", (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                    x.numel(), _stream(stream))
 
 
 def _rows(t, dtypes, name):
@@ -224,6 +255,7 @@ def _rows(t, dtypes, name):
     return ctypes.c_void_p(t.data_ptr()), t.shape[0], t.shape[1]
 
 
+@_entry
 def inv_rmsnorm(x, gamma, y, eps, stream=None):
     """y[rows,hidden] fp32 = RMSNorm(x bf16) * gamma (bf16)."""
     px, rows, hidden = _rows(x, _BF16_TYPES, "x")
@@ -232,23 +264,24 @@ def inv_rmsnorm(x, gamma, y, eps, stream=None):
         raise TypeError("gamma must be a contiguous bf16 GPU vector of length hidden")
     if (r2, h2) != (rows, hidden):
         raise ValueError("y must match x's shape")
-    _check(lib().inv_rmsnorm(px, ctypes.c_void_p(gamma.data_ptr()), py, rows, hidden,
-                             float(eps), _stream(stream)), "inv_rmsnorm")
+    return "inv_rmsnorm", (px, ctypes.c_void_p(gamma.data_ptr()), py, rows, hidden,
+                             float(eps), _stream(stream))
 
 
+@_entry
 def inv_log_softmax(x, y, stream=None):
     """y = log_softmax(x) over the last dim (fp32)."""
     px, rows, cols = _rows(x, (torch.float32,), "x")
     py, r2, c2 = _rows(y, (torch.float32,), "y")
     if (r2, c2) != (rows, cols):
         raise ValueError("y must match x's shape")
-    _check(lib().inv_log_softmax(px, py, rows, cols, _stream(stream)), "inv_log_softmax")
+    return "inv_log_softmax", (px, py, rows, cols, _stream(stream))
 
 
+@_entry
 def inv_mean(x, y, stream=None):
     """y[rows] = mean of x over the last dim (fp32)."""
     px, rows, cols = _rows(x, (torch.float32,), "x")
     if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.numel() != rows:
         raise TypeError("y must be a contiguous fp32 GPU vector with one element per row")
-    _check(lib().inv_mean(px, ctypes.c_void_p(y.data_ptr()), rows, cols, _stream(stream)),
-           "inv_mean")
+    return "inv_mean", (px, ctypes.c_void_p(y.data_ptr()), rows, cols, _stream(stream))

@@ -50,6 +50,8 @@ def lib():
     L.oracle_fold_sum_f32.restype = ctypes.c_float
     L.oracle_f32_to_bf16_rne.argtypes = [_f32p, _u16p, ctypes.c_size_t]
     L.oracle_f32_to_bf16_rne.restype = None
+    L.oracle_num_threads.argtypes = []
+    L.oracle_num_threads.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -142,3 +144,8 @@ def f32_to_bf16(x):
     y = np.empty(x.shape, np.uint16)
     lib().oracle_f32_to_bf16_rne(x.reshape(-1), y.reshape(-1), x.size)
     return y
+
+
+def num_threads():
+    """Threads the oracle's OpenMP loops run on."""
+    return int(lib().oracle_num_threads())

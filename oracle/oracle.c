@@ -30,6 +30,7 @@
  * non-associativity example.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -227,4 +228,16 @@ void oracle_f32_to_bf16_rne(const float *x, uint16_t *y, size_t n)
         else
             y[i] = (lo & 1u) ? hi : lo;
     }
+}
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
 }
