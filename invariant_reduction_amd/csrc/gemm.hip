@@ -1,35 +1,14 @@
-// Slice GEMM for gfx950: bf16 MFMA products whose K reduction follows one
-// fixed chunk tree, plus the tree combine, the atomic control and the
-// helpers the GEMM entry points need.
-//
-// The reduction of output element (i,j) (see include/detred.h):
-//   * K is cut into P chunks (P = 8, or 1 for short/odd K) of width Kc;
-//   * a chunk is one chain of v_mfma_f32_16x16x32_bf16 steps over its k in
-//     increasing order, starting from +0;
-//   * the P chunk values are added by the binary tree
-//     ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)).
-// A workgroup owns one output tile and one slice (CPS consecutive chunks,
-// a complete subtree).  It folds its chunks with a binary counter: after
-// chunk c, the running value is added to the stored left siblings for every
-// trailing one bit of c, which evaluates exactly the subtree above.  The
-// slices' roots are then added by the top levels of the same tree, either
-// by the last workgroup of a tile to finish (det), by a separate combine
-// launch (tensor-parallel shards) or by fp32 atomics (the control).
-//
-// Sources: "Reproducible LoRA Inference Through Deterministic Split-K
-// Reduction" (Highlights; Q&A: split-K partials combined by atomics versus
-// in a fixed order); arXiv 2511.17826 "Deterministic Inference across Tensor
-// Parallel Sizes..." (Abstract: one hierarchical binary tree for intra- and
-// inter-GPU reduction orders).
+// Register-staged slice GEMM engine for gfx950 (every tile shape and every
+// K, including one-chunk K with a zero-padded last MFMA step), plus the tree
+// combine, zero fill and bf16 cast kernels the GEMM entry points need.
+// The reduction order and the epilogues are shared with the LDS-DMA engine
+// through gemm_common.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace detred {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup tile description.  Waves form a WAVES_M x WAVES_N grid; each
 // wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 MFMA tiles.  K is
@@ -61,10 +40,6 @@ using TileS16 = Tile<64, 16, 4, 1, 64>;
 using TileM64 = Tile<64, 64, 2, 2, 64>;
 using TileL128 = Tile<128, 128, 2, 2, 64>;
 
-template <int N>
-struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };
-template <>
-struct Log2<1> { static constexpr int value = 0; };
 
 // Whether the top level of an 8-chunk subtree is parked in LDS (large wave
 // tiles only, where four register copies of the accumulators do not fit).
@@ -77,16 +52,6 @@ template <class T, int CPS>
 constexpr int lds_bytes()
 {
     return T::LDS_BYTES + (TopLevelInLds<T, CPS>::value ? T::WAVES * T::FM * T::FN * 64 * 16 : 0);
-}
-
-// Map the hardware workgroup id to a logical one so that consecutive logical
-// tiles land on the same XCD (workgroups are dispatched round-robin over the
-// 8 XCDs, each with its own L2).
-__device__ __forceinline__ int xcd_remap(int b, int G)
-{
-    const int xcd = b & 7, local = b >> 3;
-    const int per = G >> 3, rem = G & 7;
-    return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
 template <class T>
@@ -201,32 +166,6 @@ __device__ __forceinline__ void mma_block(f32x4 (&acc)[T::FM][T::FN], const uint
     }
 }
 
-// Element (r, c) of 16x16 tile (fm, fn) as held by a lane of the
-// v_mfma_f32_16x16x32_bf16 result: register q holds row 4*(lane/16)+q,
-// column lane%16.
-template <class T>
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[T::FM][T::FN], float* out,
-                                           long ld, int M, int N, int wrow0, int wcol0,
-                                           int lane, bool atomic)
-{
-#pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = wrow0 + fm * 16 + 4 * (lane >> 4) + q;
-                const int col = wcol0 + fn * 16 + (lane & 15);
-                if (row < M && col < N) {
-                    float* p = out + (size_t)row * ld + col;
-                    if (atomic)
-                        unsafeAtomicAdd(p, acc[fm][fn][q]);
-                    else
-                        *p = acc[fm][fn][q];
-                }
-            }
-}
-
 template <class T, int CPS, int EPI>
 __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
 {
@@ -236,15 +175,8 @@ __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-
-    // logical id -> (slice z, tile column tn, tile row tm); tile rows fastest
-    const int G = g.tiles_m * g.tiles_n * g.slices;
-    const int lid = xcd_remap(blockIdx.x, G);
-    const int tiles = g.tiles_m * g.tiles_n;
-    const int z = lid / tiles;
-    const int tl = lid % tiles;
-    const int tn = tl / g.tiles_m, tm = tl % g.tiles_m;
-    const int row0 = tm * T::BM, col0 = tn * T::BN;
+    const TileCoord tc = tile_coord(g, T::BM, T::BN);
+    const int row0 = tc.row0, col0 = tc.col0;
 
     const int wrow0 = row0 + wm * T::TM, wcol0 = col0 + wn * T::TN;
     int fm_act = (g.M - wrow0 + 15) / 16;
@@ -253,17 +185,17 @@ __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
     fn_act = fn_act < 0 ? 0 : (fn_act > T::FN ? T::FN : fn_act);
     const bool full = (fm_act == T::FM) && (fn_act == T::FN);
 
-    const int kslice = z * CPS * g.Kc;            // first k of this slice
+    const int kslice = tc.z * CPS * g.Kc;         // first k of this slice
     const int nb = (g.Kc + T::BK - 1) / T::BK;     // K blocks per chunk
     const int total = CPS * nb;
 
     f32x4 acc[T::FM][T::FN];
-    // Subtree values waiting for their right sibling.  Levels below
-    // REG_LEVELS live in registers; with 8 chunks per slice and large wave
-    // tiles the top level (held from chunk 3 to chunk 7) lives in this
-    // wave's own LDS region instead, past the two K-block stages.
+    // Subtree values waiting for their right sibling.  With 8 chunks per
+    // slice and large wave tiles the top level (held from chunk 3 to chunk
+    // 7) is parked in this wave's own LDS region, past the two stages.
     constexpr int REG_LEVELS = TopLevelInLds<T, CPS>::value ? LOG - 1 : LOG;
-    f32x4 stk[REG_LEVELS > 0 ? REG_LEVELS : 1][T::FM][T::FN];
+    constexpr int NSTK = REG_LEVELS > 0 ? REG_LEVELS : 1;
+    f32x4 stk[NSTK][T::FM][T::FN];
     f32x4* lds_top = reinterpret_cast<f32x4*>(smem + 2 * T::STAGE_ELEMS) +
                      wave * (T::FM * T::FN * 64) + lane;
     Prefetch<T> pf;
@@ -304,89 +236,11 @@ __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
                 store_block<T>(pf, smem + ((t + 1) & 1) * T::STAGE_ELEMS, tid);
             __syncthreads();
         }
-
-        // fold chunk c into the subtree: one level up per trailing one bit
-#pragma unroll
-        for (int L = 0; L < LOG; ++L) {
-            const bool in_lds = (L >= REG_LEVELS);
-            if (c & (1 << L)) {
-#pragma unroll
-                for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < T::FN; ++fn) {
-                        const f32x4 left = in_lds ? lds_top[(fm * T::FN + fn) * 64]
-                                                  : stk[in_lds ? 0 : L][fm][fn];
-                        acc[fm][fn] = left + acc[fm][fn];
-                    }
-            } else {
-#pragma unroll
-                for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < T::FN; ++fn) {
-                        if (in_lds)
-                            lds_top[(fm * T::FN + fn) * 64] = acc[fm][fn];
-                        else
-                            stk[in_lds ? 0 : L][fm][fn] = acc[fm][fn];
-                    }
-                break;
-            }
-        }
+        fold_chunk<T::FM, T::FN, LOG, REG_LEVELS, NSTK>(c, acc, stk, lds_top);
     }
     // acc now holds the root of this slice's subtree.
-
-    if (EPI == EPI_STORE) {
-        store_tile<T>(acc, g.Y + (size_t)z * g.out_z_stride, g.ldy, g.M, g.N, wrow0, wcol0,
-                      lane, false);
-        return;
-    }
-    if (EPI == EPI_ATOMIC) {
-        store_tile<T>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
-        return;
-    }
-
-    // EPI_COMBINE: publish the partial, count arrivals, and let the last
-    // slice of this tile add the partials in the fixed tree order.
-    const size_t plane = (size_t)g.M * g.N;
-    store_tile<T>(acc, g.part + (size_t)z * plane, g.N, g.M, g.N, wrow0, wcol0, lane, false);
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const unsigned prev = __hip_atomic_fetch_add(g.counters + tl, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)(8 / CPS - 1));
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __threadfence();
-
-    // a combine only exists when K has 8 chunks, so S = 8 / CPS
-    constexpr int S = 8 / CPS;
-    constexpr int VEC = T::BM * T::BN / 4;
-    for (int v = tid; v < VEC; v += T::THREADS) {
-        const int r = v / (T::BN / 4), cc = 4 * (v % (T::BN / 4));
-        const int row = row0 + r, col = col0 + cc;
-        if (row >= g.M || col >= g.N)
-            continue;
-        const float* p = g.part + (size_t)row * g.N + col;
-        float4 vals[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-            vals[s] = *reinterpret_cast<const float4*>(p + (size_t)s * plane);
-        // top levels of the tree over the S slice roots, adjacent pairs
-#pragma unroll
-        for (int w = S; w > 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < (w >> 1); ++i) {
-                vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
-                vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
-                vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
-                vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
-            }
-        *reinterpret_cast<float4*>(g.Y + (size_t)row * g.ldy + col) = vals[0];
-    }
-    if (tid == 0)
-        g.counters[tl] = 0u;  // leave the counter ready for the next call
+    finish_slice<T::BM, T::BN, T::THREADS, CPS, EPI>(acc, g, tc, wrow0, wcol0, lane, tid,
+                                                     &s_last);
 }
 
 // Y[e] = fixed tree over count arrays (count in {1,2,4,8}); 4 elements per
@@ -505,6 +359,13 @@ void tile_shape(int tile, int* bm, int* bn)
 }
 
 hipError_t launch_slice_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s)
+{
+    if (tile == TILE_L128 && lds_engine_supports(g, cps))
+        return launch_lds_gemm(epi, g, cps, s);
+    return launch_reg_gemm(tile, epi, g, cps, s);
+}
+
+hipError_t launch_reg_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (epi) {
     case EPI_STORE: return launch_tile<EPI_STORE>(tile, g, cps, s);

@@ -1,0 +1,183 @@
+// Pieces shared by the two slice-GEMM engines (register-staged and
+// LDS-DMA): tile bookkeeping, the fold of a chunk into the fixed tree, and
+// the three epilogues (direct store, last-arriver tree combine, atomics).
+//
+// The reduction every engine implements (see include/detred.h): K is cut
+// into P chunks; a chunk is a chain of v_mfma_f32_16x16x32_bf16 steps over
+// its k in increasing order from +0; the chunk values are added by the
+// binary tree ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)).  A workgroup folds the
+// chunks of its slice with a binary counter: after chunk c the running
+// value is added to the stored left sibling once per trailing one bit of c,
+// which evaluates exactly the subtree over the slice's chunks.  Sources:
+// "Reproducible LoRA Inference Through Deterministic Split-K Reduction"
+// (Highlights; Q&A) and arXiv 2511.17826 (Abstract: one hierarchical binary
+// tree for intra- and inter-GPU reduction orders).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace detred {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };
+template <>
+struct Log2<1> { static constexpr int value = 0; };
+
+// Map the hardware workgroup id to a logical one so that consecutive logical
+// tiles land on the same XCD (workgroups are dispatched round-robin over the
+// 8 XCDs, each with its own L2).  A bijection on [0, G).
+__device__ __forceinline__ int xcd_remap(int b, int G)
+{
+    const int xcd = b & 7, local = b >> 3;
+    const int per = G >> 3, rem = G & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+// Output tile and slice of this workgroup; tile rows vary fastest.
+struct TileCoord {
+    int z;          // slice (or shard) index
+    int tl;         // tile index within the slice plane
+    int row0, col0; // first output row / column of the tile
+};
+
+__device__ __forceinline__ TileCoord tile_coord(const GemmArgs& g, int bm, int bn)
+{
+    const int G = g.tiles_m * g.tiles_n * g.slices;
+    const int lid = xcd_remap(blockIdx.x, G);
+    const int tiles = g.tiles_m * g.tiles_n;
+    TileCoord t;
+    t.z = lid / tiles;
+    t.tl = lid % tiles;
+    t.row0 = (t.tl % g.tiles_m) * bm;
+    t.col0 = (t.tl / g.tiles_m) * bn;
+    return t;
+}
+
+// Store (or atomically add) a wave's FM x FN block of 16x16 MFMA results.
+// Register q of a lane holds row 4*(lane/16)+q, column lane%16 of its tile.
+template <int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], float* out, long ld,
+                                           int M, int N, int wrow0, int wcol0, int lane,
+                                           bool atomic)
+{
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = wrow0 + fm * 16 + 4 * (lane >> 4) + q;
+                const int col = wcol0 + fn * 16 + (lane & 15);
+                if (row < M && col < N) {
+                    float* p = out + (size_t)row * ld + col;
+                    if (atomic)
+                        unsafeAtomicAdd(p, acc[fm][fn][q]);
+                    else
+                        *p = acc[fm][fn][q];
+                }
+            }
+}
+
+// Fold chunk c (0-based within the slice) into the subtree.  Levels below
+// REG_LEVELS are held in registers (stk); a level at or above REG_LEVELS is
+// parked in this lane's slots of an LDS region (lds_top, one f32x4 per
+// 16x16 tile, 64 lanes apart).
+template <int FM, int FN, int LOG, int REG_LEVELS, int NSTK>
+__device__ __forceinline__ void fold_chunk(int c, f32x4 (&acc)[FM][FN],
+                                           f32x4 (&stk)[NSTK][FM][FN], f32x4* lds_top)
+{
+#pragma unroll
+    for (int L = 0; L < LOG; ++L) {
+        const bool in_lds = (L >= REG_LEVELS);
+        if (c & (1 << L)) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const f32x4 left = in_lds ? lds_top[(fm * FN + fn) * 64]
+                                              : stk[in_lds ? 0 : L][fm][fn];
+                    acc[fm][fn] = left + acc[fm][fn];
+                }
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    if (in_lds)
+                        lds_top[(fm * FN + fn) * 64] = acc[fm][fn];
+                    else
+                        stk[in_lds ? 0 : L][fm][fn] = acc[fm][fn];
+                }
+            break;
+        }
+    }
+}
+
+// Epilogue of a slice.  EPI_STORE: write the subtree root to
+// Y + z*out_z_stride.  EPI_ATOMIC: atomically add it into Y.  EPI_COMBINE:
+// write it to partial plane z, count arrivals on the tile's counter, and let
+// the last slice to arrive add the S = 8/CPS partials in the fixed tree
+// order, write Y and reset the counter.
+template <int BM, int BN, int THREADS, int CPS, int EPI, int FM, int FN>
+__device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
+                                             const TileCoord& tc, int wrow0, int wcol0,
+                                             int lane, int tid, int* s_last)
+{
+    if (EPI == EPI_STORE) {
+        store_tile<FM, FN>(acc, g.Y + (size_t)tc.z * g.out_z_stride, g.ldy, g.M, g.N, wrow0,
+                           wcol0, lane, false);
+        return;
+    }
+    if (EPI == EPI_ATOMIC) {
+        store_tile<FM, FN>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
+        return;
+    }
+    const size_t plane = (size_t)g.M * g.N;
+    store_tile<FM, FN>(acc, g.part + (size_t)tc.z * plane, g.N, g.M, g.N, wrow0, wcol0, lane,
+                       false);
+    __syncthreads();
+    constexpr int S = 8 / CPS;  // a combine only exists when K has 8 chunks
+    if (tid == 0) {
+        __threadfence();
+        const unsigned prev = __hip_atomic_fetch_add(g.counters + tc.tl, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (prev == (unsigned)(S - 1));
+    }
+    __syncthreads();
+    if (!*s_last)
+        return;
+    __threadfence();
+
+    constexpr int VEC = BM * BN / 4;
+    for (int v = tid; v < VEC; v += THREADS) {
+        const int r = v / (BN / 4), cc = 4 * (v % (BN / 4));
+        const int row = tc.row0 + r, col = tc.col0 + cc;
+        if (row >= g.M || col >= g.N)
+            continue;
+        const float* p = g.part + (size_t)row * g.N + col;
+        float4 vals[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            vals[s] = *reinterpret_cast<const float4*>(p + (size_t)s * plane);
+        // top levels of the tree over the S slice roots, adjacent pairs
+#pragma unroll
+        for (int w = S; w > 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < (w >> 1); ++i) {
+                vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
+                vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
+                vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
+                vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
+            }
+        *reinterpret_cast<float4*>(g.Y + (size_t)row * g.ldy + col) = vals[0];
+    }
+    if (tid == 0)
+        g.counters[tc.tl] = 0u;  // leave the counter ready for the next call
+}
+
+}  // namespace detred

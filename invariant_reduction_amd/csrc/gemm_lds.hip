@@ -1,0 +1,327 @@
+// LDS-DMA slice GEMM engine for gfx950: the 128x128 workgroup tile used for
+// wide outputs.  Same reduction order and epilogues as the register-staged
+// engine (gemm_common.h); only the data movement differs:
+//
+//  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
+//    STAGES K blocks of 64 in flight; the buffer descriptors' record counts
+//    turn rows past M into zeros.  These loads are issued from inline
+//    assembly (they have no register result) and waited for explicitly with
+//    s_waitcnt vmcnt + s_barrier: issued through the compiler builtin, they
+//    make every later ds_read_b64_tr_b16 wait for all outstanding loads,
+//    which would leave one stage in flight;
+//  * A (X, K-contiguous) is stored [m][k] and read as one 16-byte
+//    ds_read_b128 per MFMA operand;
+//  * B (W, N-contiguous) is stored [k][n] as loaded and read with
+//    ds_read_b64_tr_b16, which hands each lane four consecutive k of one
+//    column; two such reads form one MFMA operand;
+//  * both layouts XOR-swizzle 16-byte chunks within a row so that the
+//    fragment reads spread over the LDS banks (the DMA writes each wave's
+//    1 KiB contiguously, so the swizzle is chosen by which global chunk
+//    each lane fetches).
+//
+// Requires every 32-wide MFMA step to lie inside K (K % 32 == 0 when K is
+// one chunk; always true with 8 chunks), so no step needs zero padding.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+
+namespace detred {
+
+namespace lds {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int WAVES = 4, THREADS = 256;       // 2 x 2 waves of 64 x 64
+constexpr int TM = 64, TN = 64, FM = 4, FN = 4;
+constexpr int KSTEPS = BK / 32;
+constexpr int A_BYTES = BM * BK * 2;          // 16 KiB
+constexpr int B_BYTES = BK * BN * 2;          // 16 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int LOADS = A_BYTES / (THREADS * 16);  // 16-byte loads per lane per operand
+static_assert(LOADS == B_BYTES / (THREADS * 16), "A and B take the same number of loads");
+constexpr int PARK_BYTES = WAVES * FM * FN * 64 * 16;  // one subtree level, all waves
+constexpr int BUFFER_DWORD3 = 0x00020000;     // raw buffer, 32-bit data format
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+#define DETRED_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with only vmcnt limited (expcnt and lgkmcnt left at maximum).
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: 48-bit base, stride 0, record count in bytes.
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    i32x4 d;
+    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+    d.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.w = BUFFER_DWORD3;
+    return d;
+}
+
+// One 16-byte-per-lane load from the buffer at byte offset voff into LDS at
+// lds_base + 16*lane (lds_base wave-uniform).  Offsets at or past the record
+// count load zeros.  Completion is tracked by vmcnt only.
+__device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, const i32x4& desc)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    // m0 is written here; no compiler-generated code in these kernels
+    // keeps a value in m0 across this statement
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(desc)
+        : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Swizzle of the B tile: k-row k keeps its 16 chunks of 8 columns, with the
+// chunk index XORed by 2*h(k).  The 16 rows one transposed read touches
+// (k0 + 8g + r, r < 4, g < 4) then hit 8 distinct bank windows, twice each.
+__device__ __forceinline__ int b_swz(int k) { return 2 * ((k & 3) + 4 * ((k >> 3) & 1)); }
+
+// Fragments of one k step: A as 16-byte reads, B as two transposed reads
+// (k0..k0+3 and k0+4..k0+7 of the lane's column).
+__device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfr)[FN], const uint8_t* st,
+                                           uint32_t a_addr, const uint32_t (&b_addr)[FN], int ks)
+{
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *reinterpret_cast<const bf16x8*>(st + a_addr + fm * 16 * 8 * 16);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const uint8_t* pb = st + b_addr[fn] + ks * 32 * 256;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb + 4 * 256));
+        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bfr[fn] = __builtin_bit_cast(bf16x8, both);
+    }
+}
+
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af)[FM],
+                                         const bf16x8 (&bfr)[FN])
+{
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0,
+                                                                  0, 0);
+}
+
+// MFMA over the first nks (1 or 2) k steps of one stage, k increasing.  Both
+// steps' fragments are read before the first MFMA so the reads of step 1
+// overlap the MFMAs of step 0.  Tiles past M or N are computed too: their
+// operands are zeros or unused columns, and their results are never stored.
+__device__ __forceinline__ void mma_stage(f32x4 (&acc)[FM][FN], const uint8_t* st,
+                                          const uint32_t (&a_addr)[KSTEPS],
+                                          const uint32_t (&b_addr)[FN], int nks)
+{
+    static_assert(KSTEPS == 2, "two k steps per stage");
+    bf16x8 af0[FM], bf0[FN], af1[FM], bf1[FN];
+    load_frags(af0, bf0, st, a_addr[0], b_addr, 0);
+    load_frags(af1, bf1, st, a_addr[1], b_addr, 1);
+    mma_step(acc, af0, bf0);
+    if (nks > 1)
+        mma_step(acc, af1, bf1);
+}
+
+template <int STAGES, int CPS, int EPI, bool PARK>
+__global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
+{
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int LOG = Log2<CPS>::value;
+    constexpr int REG_LEVELS = PARK ? LOG - 1 : LOG;
+    constexpr int NSTK = REG_LEVELS > 0 ? REG_LEVELS : 1;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const TileCoord tc = tile_coord(g, BM, BN);
+    const int row0 = tc.row0, col0 = tc.col0;
+    const int wrow0 = row0 + wm * TM, wcol0 = col0 + wn * TN;
+    // a wave whose whole 64 x 64 block lies past M or N skips the MFMAs
+    const bool active = (wrow0 < g.M) && (wcol0 < g.N);
+
+    // Buffer descriptors over the tile's rows of X and columns of W.  Reads
+    // past the record count return zeros (rows >= M, the last row's
+    // columns >= N).
+    const int rows_valid = (g.M - row0) < BM ? (g.M - row0) : BM;
+    const uint16_t* xa = g.X + (size_t)row0 * g.ldx;
+    const uint16_t* wb = g.W + col0;
+    const uint32_t a_bytes = (uint32_t)(((size_t)(rows_valid - 1) * g.ldx + g.K) * 2);
+    const uint32_t b_bytes = (uint32_t)(((size_t)(g.K - 1) * g.ldw + (g.N - col0)) * 2);
+    const i32x4 ra = buffer_desc(xa, a_bytes);
+    const i32x4 rb = buffer_desc(wb, b_bytes);
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)((DETRED_LDS uint8_t*)smem);
+
+    // Per-lane byte offsets of its LOADS chunks of A and of B inside a block.
+    uint32_t offa[LOADS], offb[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int s = (wave * LOADS + i) * 64 + lane;       // 16-byte slot in the stage
+        const int r = s >> 3, ca = (s & 7) ^ (r & 7);       // A: row r, k-chunk ca
+        offa[i] = (uint32_t)((r * g.ldx + 8 * ca) * 2);
+        const int k = s >> 4, cb = (s & 15) ^ b_swz(k);     // B: k-row k, n-chunk cb
+        offb[i] = (uint32_t)((k * g.ldw + 8 * cb) * 2);
+    }
+
+    const int kslice = tc.z * CPS * g.Kc;
+    const int nb = (g.Kc + BK - 1) / BK;
+    const int total = CPS * nb;
+    const uint32_t ldw_bytes = (uint32_t)g.ldw * 2;
+
+    auto issue = [&](int t) {
+        const int kb = kslice + (t / nb) * g.Kc + (t % nb) * BK;
+        const uint32_t st = smem_lds + (uint32_t)((t % STAGES) * STAGE_BYTES) +
+                            (uint32_t)(wave * LOADS * 1024);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            dma16(st + i * 1024, offa[i] + (uint32_t)kb * 2, ra);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            dma16(st + A_BYTES + i * 1024, offb[i] + (uint32_t)kb * ldw_bytes, rb);
+    };
+
+    // Fragment addresses inside a stage.  A: row r = wm*64 + fm*16 + lane%16,
+    // k-chunk 4*ks + lane/16, swizzled by r%8 (= lane%8).  B: lane j of each
+    // 16-lane group addresses k-row k0 + j/4 (k0 = 32ks + 8g + 4q) at
+    // columns 4*(j%4) .. +3 of 16-column tile fn.
+    const int gq = lane >> 4, j = lane & 15;
+    uint32_t a_addr[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int r = wm * TM + j;
+        a_addr[ks] = (uint32_t)((r * 8 + ((4 * ks + gq) ^ (lane & 7))) * 16);
+    }
+    uint32_t b_addr[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int rr = j >> 2, p = j & 3;
+        const int k = 8 * gq + rr;                          // + 32ks + 4q added below
+        const int n = wn * TN + fn * 16 + 4 * p;
+        const int chunk = (n >> 3) ^ (2 * (rr + 4 * (gq & 1)));
+        b_addr[fn] = (uint32_t)(A_BYTES + (k * 16 + chunk) * 16 + ((n >> 2) & 1) * 8);
+    }
+
+    f32x4 acc[FM][FN];
+    f32x4 stk[NSTK][FM][FN];
+    f32x4* lds_top = reinterpret_cast<f32x4*>(smem + STAGES * STAGE_BYTES) +
+                     wave * (FM * FN * 64) + lane;
+
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+        if (p < total)
+            issue(p);
+
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int cend = kslice + (c + 1) * g.Kc;
+        for (int b = 0; b < nb; ++b) {
+            const int t = c * nb + b;
+            // stage t is complete once at most the loads of the stages issued
+            // after it are outstanding
+            if (t + STAGES - 2 < total)
+                wait_vmcnt<(STAGES - 2) * 2 * LOADS>();
+            else
+                wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + STAGES - 1 < total)
+                issue(t + STAGES - 1);
+            const int kb = kslice + c * g.Kc + b * BK;
+            int nks = (cend - kb + 31) / 32;
+            nks = nks > KSTEPS ? KSTEPS : nks;
+            const uint8_t* st = smem + (t % STAGES) * STAGE_BYTES;
+            if (active)
+                mma_stage(acc, st, a_addr, b_addr, nks);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fold_chunk<FM, FN, LOG, REG_LEVELS, NSTK>(c, acc, stk, lds_top);
+    }
+    int* s_last = reinterpret_cast<int*>(smem + STAGES * STAGE_BYTES + (PARK ? PARK_BYTES : 0));
+    finish_slice<BM, BN, THREADS, CPS, EPI>(acc, g, tc, wrow0, wcol0, lane, tid, s_last);
+}
+
+template <int CPS>
+struct Stages {
+    // with 8 chunks per slice the top subtree level is parked in LDS and
+    // fewer stages fit
+    static constexpr bool park = (CPS == 8);
+    static constexpr int value = park ? 2 : 3;
+};
+
+template <int CPS, int EPI>
+hipError_t launch(const GemmArgs& g, hipStream_t s)
+{
+    constexpr int ST = Stages<CPS>::value;
+    constexpr bool PK = Stages<CPS>::park;
+    auto fn = lds_gemm_kernel<ST, CPS, EPI, PK>;
+    constexpr int bytes = ST * STAGE_BYTES + (PK ? PARK_BYTES : 0) + 16;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr != hipSuccess)
+        return attr;
+    const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(THREADS), bytes, s, g);
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
+{
+    switch (cps) {
+    case 1: return launch<1, EPI>(g, s);
+    case 2: return launch<2, EPI>(g, s);
+    case 4: return launch<4, EPI>(g, s);
+    case 8:
+        if constexpr (EPI == EPI_COMBINE)
+            return hipErrorInvalidValue;
+        else
+            return launch<8, EPI>(g, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lds
+
+bool lds_engine_supports(const GemmArgs& g, int cps)
+{
+    (void)cps;
+    // every MFMA step inside K, and byte offsets of the tile's X rows and W
+    // columns within the 32-bit range of a buffer descriptor
+    if (g.Kc % 32 != 0)
+        return false;
+    const size_t xbytes = ((size_t)(lds::BM - 1) * g.ldx + g.K) * 2;
+    const size_t wbytes = ((size_t)g.K * g.ldw) * 2;
+    return xbytes < 0x7fffffffu && wbytes < 0x7fffffffu;
+}
+
+hipError_t launch_lds_gemm(int epi, const GemmArgs& g, int cps, hipStream_t s)
+{
+    switch (epi) {
+    case EPI_STORE: return lds::launch_cps<EPI_STORE>(g, cps, s);
+    case EPI_COMBINE: return lds::launch_cps<EPI_COMBINE>(g, cps, s);
+    case EPI_ATOMIC: return lds::launch_cps<EPI_ATOMIC>(g, cps, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace detred

@@ -26,7 +26,12 @@ struct GemmArgs {
 };
 
 void tile_shape(int tile, int* bm, int* bn);
+// Launch the slice GEMM for a tile family; TILE_L128 uses the LDS-DMA engine
+// whenever it supports the shape, else the register-staged engine.
 hipError_t launch_slice_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s);
+hipError_t launch_reg_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s);
+bool lds_engine_supports(const GemmArgs& g, int cps);
+hipError_t launch_lds_gemm(int epi, const GemmArgs& g, int cps, hipStream_t s);
 hipError_t launch_tree_combine(const float* parts, size_t stride, int count, float* Y, size_t n,
                                hipStream_t s);
 hipError_t launch_fill_zero(float* Y, long ld, int M, int N, hipStream_t s);
