@@ -9,11 +9,14 @@ vocabulary 151936), batch 256:
   cast         detred_f32_to_bf16    shrink output -> bf16
   expand       det_splitk_gemm       [256,64] B[64,4096]
   dense        det_splitk_gemm       X[256,4096] W[4096,14336]
-  tree_tp      tree_tp_gemm          X[512,8192] W[8192,8192], 8 virtual shards
+  tp_shards    tree_tp_shards_gemm   X[512,8192] W[8192,8192]: 8 virtual shards'
+                                     subtree roots (what each rank computes)
+  tp_combine   tree_combine_f32      the top 3 tree levels over the 8 roots
+                                     (what the cross-rank reduction computes)
   log_softmax  inv_log_softmax       logits[256,151936] fp32
   mean         inv_mean              logits[256,151936] fp32
 Every operation runs in libdetred's HIP kernels.  `value` is the
-deterministic GEMM work of a step (shrink, expand, dense, tree_tp) divided
+deterministic GEMM work of a step (shrink, expand, dense, tree-TP) divided
 by the step time.  Each operation is also timed alone with HIP events on the
 stream it runs on; the slowest one gets the roofline object.
 
@@ -84,7 +87,7 @@ class Workload:
         self.y_lsm = torch.empty((B, V), dtype=f32, device=dev)
         self.y_mean = torch.empty((B,), dtype=f32, device=dev)
         self.ws_shr = detred.workspace(B, R, H, 8, dev)
-        self.ws_tp = detred.workspace(TP_M, TP_N, TP_K, TP_T, dev)
+        self.p_tp = torch.empty((TP_T, TP_M, TP_N), dtype=f32, device=dev)
         dsplit = detred.policy(F, H)["default_split"]
         self.ws_dns = detred.workspace(B, F, H, dsplit, dev)
 
@@ -106,8 +109,10 @@ class Workload:
              2 * B * R * H, B * R * gb + R * H * gb + B * H * 4),
             ("dense", P(detred.det_splitk_gemm, self.X, self.W, self.y_dns, 0, self.ws_dns),
              2 * B * H * F, B * H * gb + H * F * gb + B * F * 4),
-            ("tree_tp", P(detred.tree_tp_gemm, self.Xt, self.Wt, self.y_tp, TP_T, self.ws_tp),
+            ("tp_shards", P(detred.tree_tp_shards_gemm, self.Xt, self.Wt, self.p_tp, TP_T),
              2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_M * TP_N * 4),
+            ("tp_combine", P(detred.tree_combine_f32, self.p_tp, self.y_tp),
+             0, TP_T * TP_M * TP_N * 4 + TP_M * TP_N * 4),
             ("log_softmax", P(detred.inv_log_softmax, self.lg, self.y_lsm),
              0, 2 * B * V * 4),
             ("mean", P(detred.inv_mean, self.lg, self.y_mean),
@@ -263,9 +268,13 @@ def tp_breakdown(wl, dev, stream):
 
 
 def source_hash():
+    """Hash of the kernel sources, to tell whether committed counter data
+    were taken on the kernels that run now."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "rows.hip", "api.cpp", "kernels.h"):
-        with open(os.path.join(ROOT, "invariant_reduction_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "invariant_reduction_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 

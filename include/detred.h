@@ -157,6 +157,16 @@ int tree_tp_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
                  void *ws, size_t ws_bytes, detred_stream s);
 
 /*
+ * Phase 1 of tree_tp_gemm on its own: all T shards in one launch, shard t's
+ * subtree root written to P + t*M*N as a row-major [M][N] fp32 array (ld N).
+ * P must hold T*M*N floats, 16-byte aligned.  tree_combine_f32(P, M*N, T,
+ * Y, M*N) is phase 2 (the cross-rank reduction) for a contiguous Y.
+ */
+int tree_tp_shards_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                        float *P, int M, int N, int K, int tp_shards,
+                        detred_stream s);
+
+/*
  * One shard of tree_tp_gemm at its own share shape: what rank t of a
  * T-way row-parallel group computes locally.  Xt is the rank's [M, Kt]
  * activation shard, Wt its [Kt, N] weight shard, Kt = K / T, and Pt

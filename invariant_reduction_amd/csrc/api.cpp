@@ -245,6 +245,25 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     return DETRED_OK;
 }
 
+int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* P, int M,
+                        int N, int K, int tp_shards, detred_stream s)
+{
+    int st = check_gemm(X, ldx, W, ldw, P, N, M, N, K);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = policy_for(N, K);
+    if (!pow2_le8(tp_shards) || tp_shards > p.P)
+        return DETRED_EUNSUPPORTED;
+    hipStream_t hs = (hipStream_t)s;
+    if (K == 0) {
+        const hipError_t e = launch_fill_zero(P, N, M * tp_shards, N, hs);
+        return hip_status(e);
+    }
+    GemmArgs g = make_args(p, X, ldx, W, ldw, P, N, M, N, K, tp_shards);
+    g.out_z_stride = (long)M * N;
+    return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
+}
+
 int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, float* Pt,
                        int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
 {

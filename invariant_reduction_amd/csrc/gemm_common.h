@@ -38,7 +38,12 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
     return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
-// Output tile and slice of this workgroup; tile rows vary fastest.
+// Output tile and slice of this workgroup.  Within a slice plane, tiles are
+// walked in groups of GROUP_M tile rows: rows vary fastest inside a group,
+// then columns, then groups.  The 32 workgroups an XCD runs at once then
+// cover an 8 x 4 block of tiles, whose operands overlap in that XCD's L2.
+constexpr int GROUP_M = 8;
+
 struct TileCoord {
     int z;          // slice (or shard) index
     int tl;         // tile index within the slice plane
@@ -52,9 +57,16 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& g, int bm, int b
     const int tiles = g.tiles_m * g.tiles_n;
     TileCoord t;
     t.z = lid / tiles;
-    t.tl = lid % tiles;
-    t.row0 = (t.tl % g.tiles_m) * bm;
-    t.col0 = (t.tl / g.tiles_m) * bn;
+    const int l = lid % tiles;
+    const int per_group = GROUP_M * g.tiles_n;
+    const int first_m = (l / per_group) * GROUP_M;
+    const int rows_in_group = (g.tiles_m - first_m) < GROUP_M ? (g.tiles_m - first_m) : GROUP_M;
+    const int in_group = l % per_group;
+    const int tm = first_m + in_group % rows_in_group;
+    const int tn = in_group / rows_in_group;
+    t.tl = tn * g.tiles_m + tm;  // counter slot of the tile
+    t.row0 = tm * bm;
+    t.col0 = tn * bn;
     return t;
 }
 

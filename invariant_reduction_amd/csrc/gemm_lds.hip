@@ -87,6 +87,29 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, const i3
 #pragma clang diagnostic pop
 }
 
+#ifndef DETRED_LDS_STAGES
+#define DETRED_LDS_STAGES 2
+#endif
+constexpr int SCRATCH_BYTES = 0;
+
+// s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Scheduling hint for one k step: alternate its 16 MFMAs with the 12 LDS
+// reads (4 A, 8 transposed B) of the next k step.
+__device__ __forceinline__ void interleave_reads_with_mfma()
+{
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
 // Swizzle of the B tile: k-row k keeps its 16 chunks of 8 columns, with the
 // chunk index XORed by 2*h(k).  The 16 rows one transposed read touches
 // (k0 + 8g + r, r < 4, g < 4) then hit 8 distinct bank windows, twice each.
@@ -121,29 +144,13 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af
                                                                   0, 0);
 }
 
-// MFMA over the first nks (1 or 2) k steps of one stage, k increasing.  Both
-// steps' fragments are read before the first MFMA so the reads of step 1
-// overlap the MFMAs of step 0.  Tiles past M or N are computed too: their
-// operands are zeros or unused columns, and their results are never stored.
-__device__ __forceinline__ void mma_stage(f32x4 (&acc)[FM][FN], const uint8_t* st,
-                                          const uint32_t (&a_addr)[KSTEPS],
-                                          const uint32_t (&b_addr)[FN], int nks)
-{
-    static_assert(KSTEPS == 2, "two k steps per stage");
-    bf16x8 af0[FM], bf0[FN], af1[FM], bf1[FN];
-    load_frags(af0, bf0, st, a_addr[0], b_addr, 0);
-    load_frags(af1, bf1, st, a_addr[1], b_addr, 1);
-    mma_step(acc, af0, bf0);
-    if (nks > 1)
-        mma_step(acc, af1, bf1);
-}
-
 template <int STAGES, int CPS, int EPI, bool PARK>
 __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int LOG = Log2<CPS>::value;
     constexpr int REG_LEVELS = PARK ? LOG - 1 : LOG;
+    constexpr int scratch_offset = STAGES * STAGE_BYTES + (PARK ? PARK_BYTES : 0);
     constexpr int NSTK = REG_LEVELS > 0 ? REG_LEVELS : 1;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -183,8 +190,11 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     const int total = CPS * nb;
     const uint32_t ldw_bytes = (uint32_t)g.ldw * 2;
 
+    auto block_k = [&](int t) { return kslice + (t / nb) * g.Kc + (t % nb) * BK; };
+    // LDS load of block t into stage buffer t % STAGES: LOADS_PER_ISSUE
+    // vector-memory loads per lane.
     auto issue = [&](int t) {
-        const int kb = kslice + (t / nb) * g.Kc + (t % nb) * BK;
+        const int kb = block_k(t);
         const uint32_t st = smem_lds + (uint32_t)((t % STAGES) * STAGE_BYTES) +
                             (uint32_t)(wave * LOADS * 1024);
 #pragma unroll
@@ -194,6 +204,7 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
         for (int i = 0; i < LOADS; ++i)
             dma16(st + A_BYTES + i * 1024, offb[i] + (uint32_t)kb * ldw_bytes, rb);
     };
+    constexpr int LOADS_PER_ISSUE = 2 * LOADS;
 
     // Fragment addresses inside a stage.  A: row r = wm*64 + fm*16 + lane%16,
     // k-chunk 4*ks + lane/16, swizzled by r%8 (= lane%8).  B: lane j of each
@@ -221,10 +232,29 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     f32x4* lds_top = reinterpret_cast<f32x4*>(smem + STAGES * STAGE_BYTES) +
                      wave * (FM * FN * 64) + lane;
 
+    // Software pipeline over the K blocks of the slice.  Iteration t:
+    //   first half:  MFMAs of block t, step 0 (fragments read earlier)
+    //                while step 1's fragments are read from stage t;
+    //   then:        every wave is done with stage t (lgkmcnt 0), block
+    //                t+1's loads are complete (vmcnt), barrier, and block
+    //                t+STAGES starts loading into stage t's buffer;
+    //   second half: MFMAs of block t, step 1 while step 0's fragments of
+    //                block t+1 are read.
+    // The MFMA order along k is unchanged: step 0 then step 1 of each block.
 #pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
+    for (int p = 0; p < STAGES; ++p)
         if (p < total)
             issue(p);
+    if (STAGES - 1 < total)
+        wait_vmcnt<(STAGES - 1) * LOADS_PER_ISSUE>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    if (active)
+        load_frags(fa0, fb0, smem, a_addr[0], b_addr, 0);
 
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
@@ -236,27 +266,42 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
         const int cend = kslice + (c + 1) * g.Kc;
         for (int b = 0; b < nb; ++b) {
             const int t = c * nb + b;
-            // stage t is complete once at most the loads of the stages issued
-            // after it are outstanding
-            if (t + STAGES - 2 < total)
-                wait_vmcnt<(STAGES - 2) * 2 * LOADS>();
+            const int kb = block_k(t);
+            const bool two_steps = (cend - kb) > 32;
+            const uint8_t* st = smem + (t % STAGES) * STAGE_BYTES;
+            const uint8_t* st_next = smem + ((t + 1) % STAGES) * STAGE_BYTES;
+            __builtin_amdgcn_sched_barrier(0);
+            if (active) {
+                load_frags(fa1, fb1, st, a_addr[1], b_addr, 1);
+                mma_step(acc, fa0, fb0);
+                interleave_reads_with_mfma();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkmcnt0();
+            if (t + STAGES - 1 < total)
+                wait_vmcnt<(STAGES - 2) * LOADS_PER_ISSUE>();
             else
                 wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (t + STAGES - 1 < total)
-                issue(t + STAGES - 1);
-            const int kb = kslice + c * g.Kc + b * BK;
-            int nks = (cend - kb + 31) / 32;
-            nks = nks > KSTEPS ? KSTEPS : nks;
-            const uint8_t* st = smem + (t % STAGES) * STAGE_BYTES;
-            if (active)
-                mma_stage(acc, st, a_addr, b_addr, nks);
+            if (t + STAGES < total)
+                issue(t + STAGES);
+            __builtin_amdgcn_sched_barrier(0);
+            if (active) {
+                // the next block's reads are harmless after the last block
+                if (two_steps) {
+                    load_frags(fa0, fb0, st_next, a_addr[0], b_addr, 0);
+                    mma_step(acc, fa1, fb1);
+                    interleave_reads_with_mfma();
+                } else {
+                    load_frags(fa0, fb0, st_next, a_addr[0], b_addr, 0);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         fold_chunk<FM, FN, LOG, REG_LEVELS, NSTK>(c, acc, stk, lds_top);
     }
-    int* s_last = reinterpret_cast<int*>(smem + STAGES * STAGE_BYTES + (PARK ? PARK_BYTES : 0));
+    int* s_last = reinterpret_cast<int*>(smem + scratch_offset + SCRATCH_BYTES);
     finish_slice<BM, BN, THREADS, CPS, EPI>(acc, g, tc, wrow0, wcol0, lane, tid, s_last);
 }
 
@@ -265,7 +310,7 @@ struct Stages {
     // with 8 chunks per slice the top subtree level is parked in LDS and
     // fewer stages fit
     static constexpr bool park = (CPS == 8);
-    static constexpr int value = park ? 2 : 3;
+    static constexpr int value = park ? 2 : DETRED_LDS_STAGES;
 };
 
 template <int CPS, int EPI>
@@ -274,7 +319,7 @@ hipError_t launch(const GemmArgs& g, hipStream_t s)
     constexpr int ST = Stages<CPS>::value;
     constexpr bool PK = Stages<CPS>::park;
     auto fn = lds_gemm_kernel<ST, CPS, EPI, PK>;
-    constexpr int bytes = ST * STAGE_BYTES + (PK ? PARK_BYTES : 0) + 16;
+    constexpr int bytes = ST * STAGE_BYTES + (PK ? PARK_BYTES : 0) + SCRATCH_BYTES + 16;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (attr != hipSuccess)

@@ -35,6 +35,7 @@ SIGNATURES = {
     "det_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "atomic_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "tree_tp_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "tree_tp_shards_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _P], _I),
     "tree_tp_shard_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "tree_combine_f32": ([_P, _Z, _I, _P, _Z, _P], _I),
     "detred_f32_to_bf16": ([_P, _P, _Z, _P], _I),
@@ -209,6 +210,21 @@ def tree_tp_gemm(X, W, Y, tp_shards, ws=None, stream=None):
     pws, nws = _ws(ws)
     return "tree_tp_gemm", (px, ldx, pw, ldw, py, ldy, M, N, K, tp_shards, pws, nws,
                               _stream(stream))
+
+
+@_entry
+def tree_tp_shards_gemm(X, W, P, tp_shards, stream=None):
+    """Phase 1 of tree_tp_gemm: P[t] (fp32 [T, M, N], contiguous) = shard
+    t's subtree root, all shards in one launch."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K or tuple(P.shape) != (tp_shards, M, N) or P.dtype != torch.float32 \
+            or not P.is_cuda or not P.is_contiguous():
+        raise ValueError("P must be a contiguous fp32 GPU tensor of shape (T, M, N)")
+    return "tree_tp_shards_gemm", (px, ldx, pw, ldw, ctypes.c_void_p(P.data_ptr()), M, N, K,
+                                   tp_shards, _stream(stream))
 
 
 @_entry

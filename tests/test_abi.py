@@ -110,6 +110,8 @@ def test_other_entry_points_reject():
     assert L.atomic_splitk_gemm(A16, 512, A16b, 16, A16c, 16, 16, 16, 512, 5, None) == detred.EUNSUPPORTED
     assert L.tree_tp_gemm(A16, 512, A16b, 16, A16c, 16, 16, 16, 512, 3, None, 0, None) == detred.EUNSUPPORTED
     assert L.tree_tp_gemm(A16, 512, A16b, 16, A16c, 16, 16, 16, 512, 4, None, 0, None) == detred.EWORKSPACE
+    assert L.tree_tp_shards_gemm(A16, 512, A16b, 16, A16c, 16, 16, 512, 3, None) == detred.EUNSUPPORTED
+    assert L.tree_tp_shards_gemm(None, 512, A16b, 16, A16c, 16, 16, 512, 2, None) == detred.EINVAL
     assert L.tree_tp_shard_gemm(A16, 64, A16b, 16, A16c, 16, 16, 16, 64, 6, None) == detred.EINVAL
     assert L.tree_tp_shard_gemm(A16, 40, A16b, 16, A16c, 16, 16, 16, 40, 2, None) == detred.EUNSUPPORTED
     assert L.tree_combine_f32(A16, 16, 3, A16b, 16, None) == detred.EUNSUPPORTED

@@ -102,6 +102,14 @@ def test_split_and_tp_invariance(M, N, K, dev):
         torch.cuda.synchronize()
         assert_bitwise(Y, ref, "tree_tp T=%d" % T)
         del ws
+        # phase 1 alone (all shards, one launch) then phase 2
+        P8 = torch.empty((T, M, N), dtype=torch.float32, device=dev)
+        detred.tree_tp_shards_gemm(Xd, Wd, P8, T)
+        Yp = torch.empty_like(ref)
+        detred.tree_combine_f32(P8, Yp)
+        torch.cuda.synchronize()
+        assert_bitwise(Yp, ref, "tree_tp_shards_gemm + combine, T=%d" % T)
+        del P8
         # each rank's share: X[:, Kt-slice] (copied, as a rank would hold it)
         Kt = K // T
         parts = torch.empty((T, M, N), dtype=torch.float32, device=dev)
