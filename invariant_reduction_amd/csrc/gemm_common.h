@@ -165,28 +165,45 @@ __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const G
         return;
     __threadfence();
 
+    // each thread combines VPT float4 vectors of the tile; all S*VPT loads
+    // are issued before the first addition
     constexpr int VEC = BM * BN / 4;
-    for (int v = tid; v < VEC; v += THREADS) {
-        const int r = v / (BN / 4), cc = 4 * (v % (BN / 4));
-        const int row = tc.row0 + r, col = tc.col0 + cc;
-        if (row >= g.M || col >= g.N)
-            continue;
-        const float* p = g.part + (size_t)row * g.N + col;
-        float4 vals[S];
+    constexpr int VPT = (VEC / THREADS) < 2 ? 1 : 2;
+    for (int v0 = tid; v0 < VEC; v0 += VPT * THREADS) {
+        float4 vals_all[VPT][S];
+        bool ok[VPT];
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-            vals[s] = *reinterpret_cast<const float4*>(p + (size_t)s * plane);
-        // top levels of the tree over the S slice roots, adjacent pairs
+        for (int u = 0; u < VPT; ++u) {
+            const int v = v0 + u * THREADS;
+            const int r = v / (BN / 4), cc = 4 * (v % (BN / 4));
+            const int row = tc.row0 + r, col = tc.col0 + cc;
+            ok[u] = (v < VEC) && row < g.M && col < g.N;
+            const float* p = g.part + (size_t)row * g.N + col;
 #pragma unroll
-        for (int w = S; w > 1; w >>= 1)
+            for (int s = 0; s < S; ++s)
+                vals_all[u][s] = ok[u] ? *reinterpret_cast<const float4*>(p + (size_t)s * plane)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
-            for (int i = 0; i < (w >> 1); ++i) {
-                vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
-                vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
-                vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
-                vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
-            }
-        *reinterpret_cast<float4*>(g.Y + (size_t)row * g.ldy + col) = vals[0];
+        for (int u = 0; u < VPT; ++u) {
+            if (!ok[u])
+                continue;
+            const int v = v0 + u * THREADS;
+            const int r = v / (BN / 4), cc = 4 * (v % (BN / 4));
+            float4(&vals)[S] = vals_all[u];
+            // top levels of the tree over the S slice roots, adjacent pairs
+#pragma unroll
+            for (int w = S; w > 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < (w >> 1); ++i) {
+                    vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
+                    vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
+                    vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
+                    vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
+                }
+            *reinterpret_cast<float4*>(g.Y + (size_t)(tc.row0 + r) * g.ldy + tc.col0 + cc) =
+                vals[0];
+        }
     }
     if (tid == 0)
         g.counters[tc.tl] = 0u;  // leave the counter ready for the next call

@@ -97,6 +97,7 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
 
 // -------------------------------------------------------------- log_softmax
 constexpr int ROW_THREADS = 1024;
+constexpr int UNROLL = 4;  // 16-byte loads in flight per thread
 
 // (m, s) stands for s * exp(m): a running maximum and the sum of exp(x - m)
 // of the elements seen.  Merging is commutative bit for bit: the operand
@@ -124,8 +125,7 @@ __global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
     float m = -INFINITY, s = 0.0f;
-    for (int v = threadIdx.x; v < nv; v += ROW_THREADS) {
-        const float4 q = xr[v];
+    auto visit = [&](const float4 q) {
         const float mx = fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w));
         if (mx > m) {
             s = s * expf(m - mx);
@@ -135,7 +135,21 @@ __global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x
         s = s + expf(q.y - m);
         s = s + expf(q.z - m);
         s = s + expf(q.w - m);
+    };
+    // UNROLL loads in flight per thread; vectors are still visited in the
+    // order t, t+NT, t+2NT, ...
+    int v = threadIdx.x;
+    for (; v + (UNROLL - 1) * ROW_THREADS < nv; v += UNROLL * ROW_THREADS) {
+        float4 q[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            q[u] = xr[v + u * ROW_THREADS];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            visit(q[u]);
     }
+    for (; v < nv; v += ROW_THREADS)
+        visit(xr[v]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
@@ -159,7 +173,18 @@ __global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x
     const float ls = logf(s);
 
     float4* yr = reinterpret_cast<float4*>(y + row * cols);
-    for (int v = threadIdx.x; v < nv; v += ROW_THREADS) {
+    v = threadIdx.x;
+    for (; v + (UNROLL - 1) * ROW_THREADS < nv; v += UNROLL * ROW_THREADS) {
+        float4 q[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            q[u] = xr[v + u * ROW_THREADS];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            yr[v + u * ROW_THREADS] = make_float4((q[u].x - m) - ls, (q[u].y - m) - ls,
+                                                  (q[u].z - m) - ls, (q[u].w - m) - ls);
+    }
+    for (; v < nv; v += ROW_THREADS) {
         const float4 q = xr[v];
         yr[v] = make_float4((q.x - m) - ls, (q.y - m) - ls, (q.z - m) - ls, (q.w - m) - ls);
     }
@@ -174,13 +199,24 @@ __global__ __launch_bounds__(ROW_THREADS) void mean_kernel(const float* __restri
     const float4* xr = reinterpret_cast<const float4*>(x + row * cols);
     const int nv = cols / 4;
     float s = 0.0f;
-    for (int v = threadIdx.x; v < nv; v += ROW_THREADS) {
-        const float4 q = xr[v];
+    auto visit = [&](const float4 q) {
         s = s + q.x;
         s = s + q.y;
         s = s + q.z;
         s = s + q.w;
+    };
+    int v = threadIdx.x;
+    for (; v + (UNROLL - 1) * ROW_THREADS < nv; v += UNROLL * ROW_THREADS) {
+        float4 q[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            q[u] = xr[v + u * ROW_THREADS];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            visit(q[u]);
     }
+    for (; v < nv; v += ROW_THREADS)
+        visit(xr[v]);
     s = block_sum<ROW_THREADS / 64>(s, red);
     if (threadIdx.x == 0)
         y[row] = s / (float)cols;
