@@ -122,6 +122,8 @@ int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
  * order and writes Y; one launch in total.  ws may be NULL when S == 1.
  * ws must be 256-byte aligned and at least detred_gemm_workspace_bytes()
  * large (EWORKSPACE otherwise), and its counters zero (detred_workspace_init).
+ * With S > 1, N must stay below about 4.1 million (the combine addresses a
+ * tile's rows with 32-bit offsets; EUNSUPPORTED otherwise).
  * The bits of Y do not depend on S.
  */
 int det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,

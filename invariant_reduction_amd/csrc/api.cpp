@@ -181,6 +181,9 @@ int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, floa
     GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
     if (S == 1)
         return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
+    // the last-arriver combine addresses a tile's rows with 32-bit offsets
+    if ((size_t)(p.bm - 1) * N + p.bn >= ((size_t)1 << 29))
+        return DETRED_EUNSUPPORTED;
     const size_t need = partial_bytes(M, N, S) + counter_bytes(p, M, N);
     if (!ws || !aligned256(ws) || ws_bytes < need)
         return DETRED_EWORKSPACE;

@@ -70,9 +70,25 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& g, int bm, int b
     return t;
 }
 
+// Device-scope coherence bit (sc1) of the cache-policy operand of buffer
+// loads and stores on gfx950.
+constexpr int CPOL_SC1 = 16;
+// Raw buffer descriptor word 3: 32-bit data format, no swizzle.
+constexpr int RAW_BUFFER_FLAGS = 0x00020000;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(0): every vector-memory access of this wave has completed.
+__device__ __forceinline__ void wait_vm_all()
+{
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
 // Store (or atomically add) a wave's FM x FN block of 16x16 MFMA results.
 // Register q of a lane holds row 4*(lane/16)+q, column lane%16 of its tile.
-template <int FM, int FN>
+// COHERENT stores are relaxed device-scope atomic stores: they are written
+// through to the level every XCD reads, so a workgroup on another XCD can
+// read them with device-coherent loads once they have completed.
+template <int FM, int FN, bool COHERENT = false>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], float* out, long ld,
                                            int M, int N, int wrow0, int wcol0, int lane,
                                            bool atomic)
@@ -89,6 +105,9 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], float* ou
                     float* p = out + (size_t)row * ld + col;
                     if (atomic)
                         unsafeAtomicAdd(p, acc[fm][fn][q]);
+                    else if (COHERENT)
+                        __hip_atomic_store(p, acc[fm][fn][q], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                     else
                         *p = acc[fm][fn][q];
                 }
@@ -135,6 +154,16 @@ __device__ __forceinline__ void fold_chunk(int c, f32x4 (&acc)[FM][FN],
 // write it to partial plane z, count arrivals on the tile's counter, and let
 // the last slice to arrive add the S = 8/CPS partials in the fixed tree
 // order, write Y and reset the counter.
+//
+// Ordering of the combine without whole-cache maintenance: the partials are
+// written with device-coherent stores, and each wave waits until its stores
+// have completed before the workgroup barrier that precedes the counter
+// update, so every partial of the S-1 earlier arrivals is complete before
+// the last arriver's update returns.  The last arriver issues its loads only
+// after that update has returned, and reads with device-coherent loads.  No
+// L2 write-back or invalidate is issued, so the other workgroups of the XCD
+// keep their cached operands.  Requires (BM-1)*N + BN < 2^29 (32-bit buffer
+// offsets within a tile's rows).
 template <int BM, int BN, int THREADS, int CPS, int EPI, int FM, int FN>
 __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
                                              const TileCoord& tc, int wrow0, int wcol0,
@@ -150,20 +179,27 @@ __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const G
         return;
     }
     const size_t plane = (size_t)g.M * g.N;
-    store_tile<FM, FN>(acc, g.part + (size_t)tc.z * plane, g.N, g.M, g.N, wrow0, wcol0, lane,
-                       false);
+    store_tile<FM, FN, true>(acc, g.part + (size_t)tc.z * plane, g.N, g.M, g.N, wrow0, wcol0,
+                             lane, false);
+    wait_vm_all();
     __syncthreads();
     constexpr int S = 8 / CPS;  // a combine only exists when K has 8 chunks
     if (tid == 0) {
-        __threadfence();
-        const unsigned prev = __hip_atomic_fetch_add(g.counters + tc.tl, 1u, __ATOMIC_ACQ_REL,
+        const unsigned prev = __hip_atomic_fetch_add(g.counters + tc.tl, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         *s_last = (prev == (unsigned)(S - 1));
     }
     __syncthreads();
     if (!*s_last)
         return;
-    __threadfence();
+
+    // one descriptor per partial plane, based at the tile's first element
+    __amdgpu_buffer_rsrc_t rs[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        rs[s] = __builtin_amdgcn_make_buffer_rsrc(
+            g.part + (size_t)s * plane + (size_t)tc.row0 * g.N + tc.col0, 0, 0x7fffffff,
+            RAW_BUFFER_FLAGS);
 
     // each thread combines VPT float4 vectors of the tile; all S*VPT loads
     // are issued before the first addition
@@ -176,13 +212,18 @@ __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const G
         for (int u = 0; u < VPT; ++u) {
             const int v = v0 + u * THREADS;
             const int r = v / (BN / 4), cc = 4 * (v % (BN / 4));
-            const int row = tc.row0 + r, col = tc.col0 + cc;
-            ok[u] = (v < VEC) && row < g.M && col < g.N;
-            const float* p = g.part + (size_t)row * g.N + col;
+            ok[u] = (v < VEC) && tc.row0 + r < g.M && tc.col0 + cc < g.N;
+            const int off = (r * g.N + cc) * 4;
 #pragma unroll
-            for (int s = 0; s < S; ++s)
-                vals_all[u][s] = ok[u] ? *reinterpret_cast<const float4*>(p + (size_t)s * plane)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int s = 0; s < S; ++s) {
+                float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (ok[u]) {
+                    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs[s], off, 0, CPOL_SC1);
+                    t = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                                    __uint_as_float(q.z), __uint_as_float(q.w));
+                }
+                vals_all[u][s] = t;
+            }
         }
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
