@@ -149,38 +149,24 @@ __device__ __forceinline__ void fold_chunk(int c, f32x4 (&acc)[FM][FN],
     }
 }
 
-// Epilogue of a slice.  EPI_STORE: write the subtree root to
-// Y + z*out_z_stride.  EPI_ATOMIC: atomically add it into Y.  EPI_COMBINE:
-// write it to partial plane z, count arrivals on the tile's counter, and let
-// the last slice to arrive add the S = 8/CPS partials in the fixed tree
-// order, write Y and reset the counter.
+// Arrival and combine of EPI_COMBINE, after this workgroup has issued the
+// stores of its partial (plane z of g.part) with device-coherent stores:
+// count the arrival on the tile's counter and let the last slice to arrive
+// add the S = 8/CPS partials in the fixed tree order, write Y and reset the
+// counter.
 //
-// Ordering of the combine without whole-cache maintenance: the partials are
-// written with device-coherent stores, and each wave waits until its stores
-// have completed before the workgroup barrier that precedes the counter
-// update, so every partial of the S-1 earlier arrivals is complete before
-// the last arriver's update returns.  The last arriver issues its loads only
-// after that update has returned, and reads with device-coherent loads.  No
-// L2 write-back or invalidate is issued, so the other workgroups of the XCD
-// keep their cached operands.  Requires (BM-1)*N + BN < 2^29 (32-bit buffer
-// offsets within a tile's rows).
-template <int BM, int BN, int THREADS, int CPS, int EPI, int FM, int FN>
-__device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
-                                             const TileCoord& tc, int wrow0, int wcol0,
-                                             int lane, int tid, int* s_last)
+// Ordering without whole-cache maintenance: each wave waits until its
+// partial stores have completed before the workgroup barrier that precedes
+// the counter update, so every partial of the S-1 earlier arrivals is
+// complete before the last arriver's update returns.  The last arriver
+// issues its loads only after that update has returned, and reads with
+// device-coherent loads.  No L2 write-back or invalidate is issued, so the
+// other workgroups of the XCD keep their cached operands.  Requires
+// (BM-1)*N + BN < 2^29 (32-bit buffer offsets within a tile's rows).
+template <int BM, int BN, int THREADS, int CPS>
+__device__ __forceinline__ void arrive_and_combine(const GemmArgs& g, const TileCoord& tc,
+                                                   int tid, int* s_last)
 {
-    if (EPI == EPI_STORE) {
-        store_tile<FM, FN>(acc, g.Y + (size_t)tc.z * g.out_z_stride, g.ldy, g.M, g.N, wrow0,
-                           wcol0, lane, false);
-        return;
-    }
-    if (EPI == EPI_ATOMIC) {
-        store_tile<FM, FN>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
-        return;
-    }
-    const size_t plane = (size_t)g.M * g.N;
-    store_tile<FM, FN, true>(acc, g.part + (size_t)tc.z * plane, g.N, g.M, g.N, wrow0, wcol0,
-                             lane, false);
     wait_vm_all();
     __syncthreads();
     constexpr int S = 8 / CPS;  // a combine only exists when K has 8 chunks
@@ -194,6 +180,7 @@ __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const G
         return;
 
     // one descriptor per partial plane, based at the tile's first element
+    const size_t plane = (size_t)g.M * g.N;
     __amdgpu_buffer_rsrc_t rs[S];
 #pragma unroll
     for (int s = 0; s < S; ++s)
@@ -248,6 +235,29 @@ __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const G
     }
     if (tid == 0)
         g.counters[tc.tl] = 0u;  // leave the counter ready for the next call
+}
+
+// Epilogue of a slice with per-lane stores.  EPI_STORE: write the subtree
+// root to Y + z*out_z_stride.  EPI_ATOMIC: atomically add it into Y.
+// EPI_COMBINE: write it to partial plane z with device-coherent stores, then
+// arrive_and_combine.
+template <int BM, int BN, int THREADS, int CPS, int EPI, int FM, int FN>
+__device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
+                                             const TileCoord& tc, int wrow0, int wcol0,
+                                             int lane, int tid, int* s_last)
+{
+    if (EPI == EPI_STORE) {
+        store_tile<FM, FN>(acc, g.Y + (size_t)tc.z * g.out_z_stride, g.ldy, g.M, g.N, wrow0,
+                           wcol0, lane, false);
+        return;
+    }
+    if (EPI == EPI_ATOMIC) {
+        store_tile<FM, FN>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
+        return;
+    }
+    store_tile<FM, FN, true>(acc, g.part + (size_t)tc.z * g.M * g.N, g.N, g.M, g.N, wrow0,
+                             wcol0, lane, false);
+    arrive_and_combine<BM, BN, THREADS, CPS>(g, tc, tid, s_last);
 }
 
 }  // namespace detred

@@ -144,6 +144,59 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af
                                                                   0, 0);
 }
 
+// Epilogue store through LDS.  The MFMA layout gives a lane four rows of
+// one column, so direct stores are 4-byte scatters.  Instead the workgroup's
+// 128 x 128 fp32 tile is written to the (now idle) stage buffers row-major,
+// with the 16-column group of each element XORed by (row/4)%4 so that the
+// four row groups of a 16 x 16 result land in different banks; then every
+// thread stores whole 16-byte row pieces, 32 lanes per 512-byte tile row.
+// COHERENT: device-coherent (sc1) buffer stores, for partials that another
+// workgroup combines.  Needs STAGES * STAGE_BYTES >= 64 KiB.
+template <bool COHERENT>
+__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], float* out,
+                                                   int ld, int M, int N, int row0, int col0,
+                                                   int wm, int wn, int lane, int tid,
+                                                   uint8_t* smem)
+{
+    float* t = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done with the stage buffers
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = wm * TM + fm * 16 + 4 * (lane >> 4) + q;
+                const int c = wn * TN + fn * 16 + (lane & 15);
+                t[r * BN + (c ^ (16 * ((r >> 2) & 3)))] = acc[fm][fn][q];
+            }
+    __syncthreads();
+    // Stores go through a raw buffer based at the tile's first element; a
+    // piece outside M x N gets an offset past the record count, and the
+    // hardware drops it, so the loop has no branch and the reads above stay
+    // batched.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        out + (size_t)row0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+    // all of a thread's row pieces are read before the first store
+    constexpr int ITER = BM * BN / 4 / THREADS;
+    static_assert(ITER * THREADS * 4 == BM * BN, "whole float4 pieces per thread");
+    u32x4 val[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int v = tid + i * THREADS;
+        const int r = v / (BN / 4), c4 = v % (BN / 4);
+        val[i] = *reinterpret_cast<const u32x4*>(t + r * BN + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
+    }
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int v = tid + i * THREADS;
+        const int r = v / (BN / 4), c4 = v % (BN / 4);
+        const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
+        const int off = in ? (r * ld + 4 * c4) * 4 : (int)0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, COHERENT ? CPOL_SC1 : 0);
+    }
+}
+
 template <int STAGES, int CPS, int EPI, bool PARK>
 __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
 {
@@ -301,9 +354,29 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
         }
         fold_chunk<FM, FN, LOG, REG_LEVELS, NSTK>(c, acc, stk, lds_top);
     }
-    int* s_last = reinterpret_cast<int*>(smem + scratch_offset + SCRATCH_BYTES);
-    finish_slice<BM, BN, THREADS, CPS, EPI>(acc, g, tc, wrow0, wcol0, lane, tid, s_last);
+    if constexpr (EPI == EPI_ATOMIC) {
+        store_tile<FM, FN>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
+    } else {
+        float* out;
+        int ld;
+        if constexpr (EPI == EPI_STORE) {
+            out = g.Y + (size_t)tc.z * g.out_z_stride;
+            ld = g.ldy;
+        } else {
+            out = g.part + (size_t)tc.z * g.M * g.N;
+            ld = g.N;
+        }
+        store_tile_via_lds<EPI == EPI_COMBINE>(acc, out, ld, g.M, g.N, row0, col0, wm, wn,
+                                               lane, tid, smem);
+        if constexpr (EPI == EPI_COMBINE) {
+            int* s_last = reinterpret_cast<int*>(smem + scratch_offset + SCRATCH_BYTES);
+            arrive_and_combine<BM, BN, THREADS, CPS>(g, tc, tid, s_last);
+        }
+    }
 }
+
+static_assert(DETRED_LDS_STAGES * STAGE_BYTES >= BM * BN * 4 && 2 * STAGE_BYTES >= BM * BN * 4,
+              "the epilogue stages the fp32 tile in the stage buffers");
 
 template <int CPS>
 struct Stages {
@@ -350,13 +423,17 @@ hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 bool lds_engine_supports(const GemmArgs& g, int cps)
 {
     (void)cps;
-    // every MFMA step inside K, and byte offsets of the tile's X rows and W
-    // columns within the 32-bit range of a buffer descriptor
+    // every MFMA step inside K, and byte offsets of the tile's X rows, W
+    // columns and output rows within the 31-bit record range of a buffer
+    // descriptor
     if (g.Kc % 32 != 0)
         return false;
     const size_t xbytes = ((size_t)(lds::BM - 1) * g.ldx + g.K) * 2;
     const size_t wbytes = ((size_t)g.K * g.ldw) * 2;
-    return xbytes < 0x7fffffffu && wbytes < 0x7fffffffu;
+    // output rows of the tile (Y at ldy, or partial planes at N) likewise
+    const size_t ld = (size_t)(g.ldy > g.N ? g.ldy : g.N);
+    const size_t ybytes = ((lds::BM - 1) * ld + lds::BN) * 4;
+    return xbytes < 0x7fffffffu && wbytes < 0x7fffffffu && ybytes < 0x7fffffffu;
 }
 
 hipError_t launch_lds_gemm(int epi, const GemmArgs& g, int cps, hipStream_t s)
