@@ -110,7 +110,7 @@ class Workload:
             ("dense", P(detred.det_splitk_gemm, self.X, self.W, self.y_dns, 0, self.ws_dns),
              2 * B * H * F, B * H * gb + H * F * gb + B * F * 4),
             ("tp_shards", P(detred.tree_tp_shards_gemm, self.Xt, self.Wt, self.p_tp, TP_T),
-             2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_M * TP_N * 4),
+             2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_T * TP_M * TP_N * 4),
             ("tp_combine", P(detred.tree_combine_f32, self.p_tp, self.y_tp),
              0, TP_T * TP_M * TP_N * 4 + TP_M * TP_N * 4),
             ("log_softmax", P(detred.inv_log_softmax, self.lg, self.y_lsm),

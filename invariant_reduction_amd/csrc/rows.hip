@@ -22,6 +22,8 @@
 
 namespace detred {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -96,8 +98,18 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
 }
 
 // -------------------------------------------------------------- log_softmax
-constexpr int ROW_THREADS = 1024;
-constexpr int UNROLL = 4;  // 16-byte loads in flight per thread
+// The row is read in the first pass and needed again in the second.  Most of
+// it stays on chip in between: a thread keeps its first LSM_REG vectors in
+// registers and its next LSM_LDS vectors in LDS (with 512 threads that is
+// 40 + 18 vectors, 464 KiB of a row, 78% of a 151936-wide row); only the
+// rest is read from memory a second time.  The visit order is that of
+// every row kernel here (thread t: vectors t, t+NT, t+2NT, ...).
+constexpr int ROW_THREADS = 1024;  // mean
+constexpr int UNROLL = 4;          // 16-byte loads in flight per thread
+constexpr int LSM_THREADS = 512;
+constexpr int LSM_REG = 40;
+constexpr int LSM_LDS = 18;
+constexpr int LSM_LDS_BYTES = LSM_LDS * LSM_THREADS * 16;
 
 // (m, s) stands for s * exp(m): a running maximum and the sum of exp(x - m)
 // of the elements seen.  Merging is commutative bit for bit: the operand
@@ -115,14 +127,27 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
     }
 }
 
-__global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x, float* y,
+// y = (x - m) - ls.  The output is written once and not read back here, so
+// it is stored non-temporally: it does not push the logits (or other data
+// that is read again) out of the caches.
+__device__ __forceinline__ void store_shifted(float4* p, const float4 q, float m, float ls)
+{
+    f32x4 r = {(q.x - m) - ls, (q.y - m) - ls, (q.z - m) - ls, (q.w - m) - ls};
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+}
+
+__global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x, float* y,
                                                                   int cols)
 {
-    __shared__ float red_m[ROW_THREADS / 64], red_s[ROW_THREADS / 64];
+    extern __shared__ float4 cache[];  // LSM_LDS vectors per thread
+    __shared__ float red_m[LSM_THREADS / 64], red_s[LSM_THREADS / 64];
+    constexpr int NT = LSM_THREADS;
+    const int tid = threadIdx.x;
     const size_t row = blockIdx.x;
     const float4* xr = reinterpret_cast<const float4*>(x + row * cols);
+    float4* yr = reinterpret_cast<float4*>(y + row * cols);
     const int nv = cols / 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
 
     float m = -INFINITY, s = 0.0f;
     auto visit = [&](const float4 q) {
@@ -136,20 +161,52 @@ __global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x
         s = s + expf(q.z - m);
         s = s + expf(q.w - m);
     };
-    // UNROLL loads in flight per thread; vectors are still visited in the
-    // order t, t+NT, t+2NT, ...
-    int v = threadIdx.x;
-    for (; v + (UNROLL - 1) * ROW_THREADS < nv; v += UNROLL * ROW_THREADS) {
+
+    // vectors 0 .. LSM_REG-1 of the thread: all loads issued, then visited
+    float4 rc[LSM_REG];
+#pragma unroll
+    for (int i = 0; i < LSM_REG; ++i) {
+        const int v = tid + i * NT;
+        rc[i] = (v < nv) ? xr[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < LSM_REG; ++i)
+        if (tid + i * NT < nv)
+            visit(rc[i]);
+    // the next LSM_LDS vectors, kept in LDS, UNROLL loads in flight
+#pragma unroll
+    for (int i0 = 0; i0 < LSM_LDS; i0 += UNROLL) {
+        float4 q[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int v = tid + (LSM_REG + i0 + u) * NT;
+            if (i0 + u < LSM_LDS && v < nv)
+                q[u] = xr[v];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int v = tid + (LSM_REG + i0 + u) * NT;
+            if (i0 + u < LSM_LDS && v < nv) {
+                cache[(i0 + u) * NT + tid] = q[u];
+                visit(q[u]);
+            }
+        }
+    }
+    // the rest of the row, streamed
+    constexpr int CACHED = LSM_REG + LSM_LDS;
+    int v = tid + CACHED * NT;
+    for (; v + (UNROLL - 1) * NT < nv; v += UNROLL * NT) {
         float4 q[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            q[u] = xr[v + u * ROW_THREADS];
+            q[u] = xr[v + u * NT];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
             visit(q[u]);
     }
-    for (; v < nv; v += ROW_THREADS)
+    for (; v < nv; v += NT)
         visit(xr[v]);
+
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
@@ -160,7 +217,7 @@ __global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x
         red_s[wave] = s;
     }
     __syncthreads();
-    constexpr int NW = ROW_THREADS / 64;
+    constexpr int NW = LSM_THREADS / 64;
     m = (lane < NW) ? red_m[lane] : -INFINITY;
     s = (lane < NW) ? red_s[lane] : 0.0f;
 #pragma unroll
@@ -172,22 +229,31 @@ __global__ __launch_bounds__(ROW_THREADS) void log_softmax_kernel(const float* x
     s = __shfl(s, 0, 64);
     const float ls = logf(s);
 
-    float4* yr = reinterpret_cast<float4*>(y + row * cols);
-    v = threadIdx.x;
-    for (; v + (UNROLL - 1) * ROW_THREADS < nv; v += UNROLL * ROW_THREADS) {
+    // second pass: cached vectors from registers and LDS, the rest re-read
+#pragma unroll
+    for (int i = 0; i < LSM_REG; ++i) {
+        const int w = tid + i * NT;
+        if (w < nv)
+            store_shifted(yr + w, rc[i], m, ls);
+    }
+#pragma unroll
+    for (int i = 0; i < LSM_LDS; ++i) {
+        const int w = tid + (LSM_REG + i) * NT;
+        if (w < nv)
+            store_shifted(yr + w, cache[i * NT + tid], m, ls);
+    }
+    v = tid + CACHED * NT;
+    for (; v + (UNROLL - 1) * NT < nv; v += UNROLL * NT) {
         float4 q[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            q[u] = xr[v + u * ROW_THREADS];
+            q[u] = xr[v + u * NT];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            yr[v + u * ROW_THREADS] = make_float4((q[u].x - m) - ls, (q[u].y - m) - ls,
-                                                  (q[u].z - m) - ls, (q[u].w - m) - ls);
+            store_shifted(yr + v + u * NT, q[u], m, ls);
     }
-    for (; v < nv; v += ROW_THREADS) {
-        const float4 q = xr[v];
-        yr[v] = make_float4((q.x - m) - ls, (q.y - m) - ls, (q.z - m) - ls, (q.w - m) - ls);
-    }
+    for (; v < nv; v += NT)
+        store_shifted(yr + v, xr[v], m, ls);
 }
 
 // --------------------------------------------------------------------- mean
@@ -232,7 +298,13 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, in
 
 hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s)
 {
-    hipLaunchKernelGGL(log_softmax_kernel, dim3(rows), dim3(ROW_THREADS), 0, s, x, y, cols);
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(log_softmax_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, LSM_LDS_BYTES);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL(log_softmax_kernel, dim3(rows), dim3(LSM_THREADS), LSM_LDS_BYTES, s, x, y,
+                       cols);
     return hipGetLastError();
 }
 
