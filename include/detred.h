@@ -78,6 +78,9 @@ typedef enum {
 
 typedef void *detred_stream; /* hipStream_t; NULL = null stream */
 
+/* Element type of an output that may be fp32 or bf16. */
+enum { DETRED_F32 = 0, DETRED_BF16 = 1 };
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *detred_status_string(int status);
 
@@ -129,6 +132,58 @@ int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
 int det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
                     float *Y, int ldy, int M, int N, int K, int split_k,
                     void *ws, size_t ws_bytes, detred_stream s);
+
+/*
+ * Deterministic addmm, the form of torch.addmm that the "Batch Invariant Ops"
+ * project makes batch invariant (Highlighted Details), with an optional bf16
+ * output:
+ *   p = the canonical product of X[M,K] and W[K,N] (the bits det_splitk_gemm
+ *       writes, for any split_k);
+ *   y = beta*C[i][j] + alpha*p   (C == NULL: y = alpha*p), each product and
+ *       the sum rounded to binary32 as written (alpha = beta = 1 makes both
+ *       products exact);
+ *   Y[i][j] = y as fp32 (y_dtype DETRED_F32) or rounded to bf16, nearest
+ *       even (DETRED_BF16; NaN stays NaN).
+ * C is fp32, 16-byte aligned; ldc = 0 broadcasts one row of N values (a
+ * bias) to every row, otherwise ldc >= N and ldc % 4 == 0.  Y is 16-byte
+ * aligned, ldy % 4 == 0, in elements of y_dtype.  The epilogue is applied
+ * where the final value of an element is written (after the tree combine
+ * when split_k > 1), so it adds no pass over Y.  split_k, ws and errors as
+ * det_splitk_gemm; EINVAL for a bad y_dtype, C or ldc.  K == 0 gives
+ * y = beta*C + alpha*(+0).  Row i of Y depends only on row i of X (and of C).
+ */
+int det_splitk_addmm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                     const float *C, int ldc, float alpha, float beta,
+                     void *Y, int ldy, int y_dtype, int M, int N, int K,
+                     int split_k, void *ws, size_t ws_bytes, detred_stream s);
+
+/*
+ * Workspace of det_lora_forward for an M x N layer output with input width K
+ * and LoRA rank r: the fp32 base product, the fp32 shrink output, its bf16
+ * cast and the split-K workspaces of the base product and the shrink, each
+ * 256-byte aligned.  0 for invalid arguments.
+ */
+size_t det_lora_workspace_bytes(int M, int N, int K, int r);
+
+/*
+ * A LoRA-adapted linear layer in one call, every step in a fixed order
+ * (split-K paper, Highlights and Q&A: the base product, the shrink X*A and
+ * the expand of its bf16 cast by B):
+ *   base = det_splitk_gemm(X, W)              fp32 [M,N], policy split;
+ *   z    = det_splitk_gemm(X, A)              fp32 [M,r], policy split (8);
+ *   zb   = detred_f32_to_bf16(z)              bf16 [M,r];
+ *   Y    = det_splitk_addmm(zb, B, C = base, alpha = scale, beta = 1,
+ *                           bf16 output)      bf16 [M,N]
+ * i.e. Y = bf16(base + scale*(zb*B)).  X [M,K] ld ldx, W [K,N] ld ldw,
+ * A [K,r] ld lda, B [r,N] ld ldb, all bf16; Y bf16 ld ldy.  r % 8 == 0,
+ * K % 8 == 0, N % 8 == 0.  ws: det_lora_workspace_bytes(M,N,K,r) bytes,
+ * 256-byte aligned, zeroed once with detred_workspace_init.  Four launches
+ * on s.  The bits of Y do not depend on M.
+ */
+int det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                     const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                     float scale, uint16_t *Y, int ldy, int M, int N, int K,
+                     int r, void *ws, size_t ws_bytes, detred_stream s);
 
 /*
  * The nondeterministic control: the same slice products as det_splitk_gemm,
@@ -210,6 +265,14 @@ int detred_f32_to_bf16(const float *x, uint16_t *y, size_t n, detred_stream s);
  */
 int inv_rmsnorm(const uint16_t *x, const uint16_t *gamma, float *y, int rows,
                 int hidden, float eps, detred_stream s);
+
+/*
+ * inv_rmsnorm with a bf16 output: the same binary32 values, each rounded to
+ * bf16 (nearest even) as it is stored.  y bf16 [rows][hidden], 16-byte
+ * aligned; other arguments and errors as inv_rmsnorm.
+ */
+int inv_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, uint16_t *y,
+                     int rows, int hidden, float eps, detred_stream s);
 
 /*
  * Batch-invariant log_softmax over the last dimension (Batch Invariant Ops,

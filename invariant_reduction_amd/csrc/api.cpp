@@ -100,6 +100,12 @@ GemmArgs make_args(const Policy& p, const uint16_t* X, int ldx, const uint16_t* 
     g.slices = slices;
     g.tiles_m = (M + p.bm - 1) / p.bm;
     g.tiles_n = (N + p.bn - 1) / p.bn;
+    g.epi = 0;
+    g.C = nullptr;
+    g.ldc = 0;
+    g.alpha = 1.0f;
+    g.beta = 1.0f;
+    g.out_bf16 = 0;
     return g;
 }
 
@@ -165,6 +171,79 @@ int detred_workspace_init(void* ws, size_t ws_bytes, detred_stream s)
     return hip_status(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)s));
 }
 
+}  // extern "C"
+
+namespace {
+
+// The deterministic product (and its epilogue, when g.epi) with S slices:
+// one launch; with S > 1 the partials and counters live in ws.
+int run_det(const Policy& p, GemmArgs g, int S, void* ws, size_t ws_bytes, hipStream_t hs)
+{
+    if (g.K == 0)
+        return hip_status(g.epi ? launch_epilogue_only(g, hs)
+                                : launch_fill_zero(g.Y, g.ldy, g.M, g.N, hs));
+    if (S == 1)
+        return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
+    // the last-arriver combine addresses a tile's rows with 32-bit offsets
+    if ((size_t)(p.bm - 1) * g.N + p.bn >= ((size_t)1 << 29))
+        return DETRED_EUNSUPPORTED;
+    const size_t need = partial_bytes(g.M, g.N, S) + counter_bytes(p, g.M, g.N);
+    if (!ws || !aligned256(ws) || ws_bytes < need)
+        return DETRED_EWORKSPACE;
+    g.part = (float*)ws;
+    g.counters = (unsigned*)((char*)ws + partial_bytes(g.M, g.N, S));
+    return hip_status(launch_slice_gemm(p.tile, EPI_COMBINE, g, p.P / S, hs));
+}
+
+// Validation of det_splitk_gemm / det_splitk_addmm that would otherwise
+// only happen in run_det (so a composite call can check before launching).
+int check_det(const Policy& p, int M, int N, int K, int S, const void* ws, size_t ws_bytes)
+{
+    if (K == 0 || S == 1)
+        return DETRED_OK;
+    if ((size_t)(p.bm - 1) * N + p.bn >= ((size_t)1 << 29))
+        return DETRED_EUNSUPPORTED;
+    if (!ws || !aligned256(ws) || ws_bytes < partial_bytes(M, N, S) + counter_bytes(p, M, N))
+        return DETRED_EWORKSPACE;
+    return DETRED_OK;
+}
+
+int check_epilogue(const float* C, int ldc, int N, int y_dtype)
+{
+    if (y_dtype != DETRED_F32 && y_dtype != DETRED_BF16)
+        return DETRED_EINVAL;
+    if (C && (!aligned16(C) || ldc < 0 || (ldc != 0 && (ldc < N || ldc % 4 != 0))))
+        return DETRED_EINVAL;
+    return DETRED_OK;
+}
+
+// Byte layout of the det_lora_forward workspace.
+struct LoraLayout {
+    size_t base, z, zb, ws_base, ws_z, total;
+    size_t ws_base_bytes, ws_z_bytes;
+    int s_base, s_z;
+};
+
+LoraLayout lora_layout(int M, int N, int K, int r)
+{
+    LoraLayout l;
+    l.s_base = policy_for(N, K).default_split;
+    l.s_z = policy_for(r, K).default_split;
+    l.ws_base_bytes = detred_gemm_workspace_bytes(M, N, K, l.s_base);
+    l.ws_z_bytes = detred_gemm_workspace_bytes(M, r, K, l.s_z);
+    l.base = 0;
+    l.z = l.base + round_up((size_t)M * N * sizeof(float), 256);
+    l.zb = l.z + round_up((size_t)M * r * sizeof(float), 256);
+    l.ws_base = l.zb + round_up((size_t)M * r * sizeof(uint16_t), 256);
+    l.ws_z = l.ws_base + round_up(l.ws_base_bytes, 256);
+    l.total = l.ws_z + round_up(l.ws_z_bytes, 256);
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
 int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
                     int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
 {
@@ -175,21 +254,84 @@ int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, floa
     int S = 0;
     if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
         return st;
-    hipStream_t hs = (hipStream_t)s;
-    if (K == 0)
-        return hip_status(launch_fill_zero(Y, ldy, M, N, hs));
-    GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
-    if (S == 1)
-        return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
-    // the last-arriver combine addresses a tile's rows with 32-bit offsets
-    if ((size_t)(p.bm - 1) * N + p.bn >= ((size_t)1 << 29))
+    const GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
+    return run_det(p, g, S, ws, ws_bytes, (hipStream_t)s);
+}
+
+int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* C,
+                     int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype, int M, int N,
+                     int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+{
+    int st = check_epilogue(C, ldc, N, y_dtype);
+    if (st != DETRED_OK)
+        return st;
+    st = check_gemm(X, ldx, W, ldw, (const float*)Y, ldy, M, N, K);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = policy_for(N, K);
+    int S = 0;
+    if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
+        return st;
+    GemmArgs g = make_args(p, X, ldx, W, ldw, (float*)Y, ldy, M, N, K, S);
+    g.epi = 1;
+    g.C = C;
+    g.ldc = ldc;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.out_bf16 = (y_dtype == DETRED_BF16);
+    return run_det(p, g, S, ws, ws_bytes, (hipStream_t)s);
+}
+
+size_t det_lora_workspace_bytes(int M, int N, int K, int r)
+{
+    if (M < 0 || N < 0 || K < 0 || r <= 0)
+        return 0;
+    return lora_layout(M, N, K, r).total;
+}
+
+int det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const uint16_t* A,
+                     int lda, const uint16_t* B, int ldb, float scale, uint16_t* Y, int ldy, int M,
+                     int N, int K, int r, void* ws, size_t ws_bytes, detred_stream s)
+{
+    if (M < 0 || N < 0 || K < 0 || r <= 0)
+        return DETRED_EINVAL;
+    if (r % 8 != 0)
         return DETRED_EUNSUPPORTED;
-    const size_t need = partial_bytes(M, N, S) + counter_bytes(p, M, N);
-    if (!ws || !aligned256(ws) || ws_bytes < need)
+    if (M == 0 || N == 0)
+        return DETRED_OK;
+    const LoraLayout l = lora_layout(M, N, K, r);
+    if (!ws || !aligned256(ws) || ws_bytes < l.total)
         return DETRED_EWORKSPACE;
-    g.part = (float*)ws;
-    g.counters = (unsigned*)((char*)ws + partial_bytes(M, N, S));
-    return hip_status(launch_slice_gemm(p.tile, EPI_COMBINE, g, p.P / S, hs));
+    char* w = (char*)ws;
+    float* base = (float*)(w + l.base);
+    float* z = (float*)(w + l.z);
+    uint16_t* zb = (uint16_t*)(w + l.zb);
+    const Policy pb = policy_for(N, K), pz = policy_for(r, K), pe = policy_for(N, r);
+    // every check before the first launch
+    int st;
+    if ((st = check_gemm(X, ldx, W, ldw, base, N, M, N, K)) != DETRED_OK ||
+        (st = check_gemm(X, ldx, A, lda, z, r, M, r, K)) != DETRED_OK ||
+        (st = check_gemm(zb, r, B, ldb, (const float*)Y, ldy, M, N, r)) != DETRED_OK ||
+        (st = check_det(pb, M, N, K, l.s_base, w + l.ws_base, l.ws_base_bytes)) != DETRED_OK ||
+        (st = check_det(pz, M, r, K, l.s_z, w + l.ws_z, l.ws_z_bytes)) != DETRED_OK)
+        return st;
+    hipStream_t hs = (hipStream_t)s;
+    const GemmArgs gb = make_args(pb, X, ldx, W, ldw, base, N, M, N, K, l.s_base);
+    if ((st = run_det(pb, gb, l.s_base, w + l.ws_base, l.ws_base_bytes, hs)) != DETRED_OK)
+        return st;
+    const GemmArgs gz = make_args(pz, X, ldx, A, lda, z, r, M, r, K, l.s_z);
+    if ((st = run_det(pz, gz, l.s_z, w + l.ws_z, l.ws_z_bytes, hs)) != DETRED_OK)
+        return st;
+    if (launch_cast_bf16(z, zb, (size_t)M * r, hs) != hipSuccess)
+        return DETRED_EHIP;
+    GemmArgs ge = make_args(pe, zb, r, B, ldb, (float*)Y, ldy, M, N, r, 1);
+    ge.epi = 1;
+    ge.C = base;
+    ge.ldc = N;
+    ge.alpha = scale;
+    ge.beta = 1.0f;
+    ge.out_bf16 = 1;
+    return run_det(pe, ge, 1, nullptr, 0, hs);
 }
 
 int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
@@ -326,6 +468,20 @@ int inv_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows, in
     if (hidden == 0 || hidden % 8 != 0 || hidden > 65536)
         return DETRED_EUNSUPPORTED;
     return hip_status(launch_rmsnorm(x, gamma, y, rows, hidden, eps, (hipStream_t)s));
+}
+
+int inv_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int rows, int hidden,
+                     float eps, detred_stream s)
+{
+    if (rows < 0 || hidden < 0)
+        return DETRED_EINVAL;
+    if (rows == 0)
+        return DETRED_OK;
+    if (!x || !gamma || !y || !aligned16(x) || !aligned16(gamma) || !aligned16(y))
+        return DETRED_EINVAL;
+    if (hidden == 0 || hidden % 8 != 0 || hidden > 65536)
+        return DETRED_EUNSUPPORTED;
+    return hip_status(launch_rmsnorm_bf16(x, gamma, y, rows, hidden, eps, (hipStream_t)s));
 }
 
 int inv_log_softmax(const float* x, float* y, int rows, int cols, detred_stream s)

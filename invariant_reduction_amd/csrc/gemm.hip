@@ -281,15 +281,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* Y, long ld, int M
     }
 }
 
-// binary32 -> bf16, nearest even; NaN -> quiet NaN of the same sign.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ x,
                                                         uint16_t* __restrict__ y, size_t n8)
 {
@@ -304,6 +295,16 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
         o.w = f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16);
         reinterpret_cast<uint4*>(y)[v] = o;
     }
+}
+
+// The addmm of an empty product (K = 0): every element is the epilogue of
+// p = +0.  One thread per element, grid-stride.
+__global__ __launch_bounds__(256) void epilogue_only_kernel(GemmArgs g)
+{
+    const size_t n = (size_t)g.M * g.N;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (size_t)gridDim.x * blockDim.x)
+        write_final1(g, (int)(e / g.N), (int)(e % g.N), 0.0f);
 }
 
 // ---------------------------------------------------------------- launches
@@ -402,6 +403,13 @@ hipError_t launch_fill_zero(float* Y, long ld, int M, int N, hipStream_t s)
 {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((size_t)M * (N / 4), 256)), dim3(256), 0,
                        s, Y, ld, M, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_epilogue_only(const GemmArgs& g, hipStream_t s)
+{
+    const size_t n = (size_t)g.M * g.N;
+    hipLaunchKernelGGL(epilogue_only_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bf16.h"
 #include "kernels.h"
 
 namespace detred {
@@ -149,6 +150,51 @@ __device__ __forceinline__ void fold_chunk(int c, f32x4 (&acc)[FM][FN],
     }
 }
 
+// The final value of output element(s) under the epilogue of g (g.epi set):
+// y = beta*c + alpha*p, or alpha*p without C; each operation rounds.
+__device__ __forceinline__ float epi_value(const GemmArgs& g, float p, float c)
+{
+    const float ap = g.alpha * p;
+    return g.C ? g.beta * c + ap : ap;
+}
+
+// Write the final value of element (row, col) of Y from its product p.
+__device__ __forceinline__ void write_final1(const GemmArgs& g, int row, int col, float p)
+{
+    if (!g.epi) {
+        g.Y[(size_t)row * g.ldy + col] = p;
+        return;
+    }
+    const float c = g.C ? g.C[(size_t)row * g.ldc + col] : 0.0f;
+    const float y = epi_value(g, p, c);
+    if (g.out_bf16)
+        reinterpret_cast<uint16_t*>(g.Y)[(size_t)row * g.ldy + col] = (uint16_t)f32_to_bf16_bits(y);
+    else
+        g.Y[(size_t)row * g.ldy + col] = y;
+}
+
+// The same for elements (row, col .. col+3), all inside M x N.
+__device__ __forceinline__ void write_final4(const GemmArgs& g, int row, int col, float4 p)
+{
+    if (!g.epi) {
+        *reinterpret_cast<float4*>(g.Y + (size_t)row * g.ldy + col) = p;
+        return;
+    }
+    float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g.C)
+        c = *reinterpret_cast<const float4*>(g.C + (size_t)row * g.ldc + col);
+    const float4 y = make_float4(epi_value(g, p.x, c.x), epi_value(g, p.y, c.y),
+                                 epi_value(g, p.z, c.z), epi_value(g, p.w, c.w));
+    if (g.out_bf16) {
+        uint2 o;
+        o.x = f32_to_bf16_bits(y.x) | (f32_to_bf16_bits(y.y) << 16);
+        o.y = f32_to_bf16_bits(y.z) | (f32_to_bf16_bits(y.w) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.Y) + (size_t)row * g.ldy + col) = o;
+    } else {
+        *reinterpret_cast<float4*>(g.Y + (size_t)row * g.ldy + col) = y;
+    }
+}
+
 // Arrival and combine of EPI_COMBINE, after this workgroup has issued the
 // stores of its partial (plane z of g.part) with device-coherent stores:
 // count the arrival on the tile's counter and let the last slice to arrive
@@ -229,8 +275,7 @@ __device__ __forceinline__ void arrive_and_combine(const GemmArgs& g, const Tile
                     vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
                     vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
                 }
-            *reinterpret_cast<float4*>(g.Y + (size_t)(tc.row0 + r) * g.ldy + tc.col0 + cc) =
-                vals[0];
+            write_final4(g, tc.row0 + r, tc.col0 + cc, vals[0]);
         }
     }
     if (tid == 0)
@@ -238,7 +283,8 @@ __device__ __forceinline__ void arrive_and_combine(const GemmArgs& g, const Tile
 }
 
 // Epilogue of a slice with per-lane stores.  EPI_STORE: write the subtree
-// root to Y + z*out_z_stride.  EPI_ATOMIC: atomically add it into Y.
+// root to Y + z*out_z_stride (through the output epilogue when g.epi, which
+// only single-slice calls set).  EPI_ATOMIC: atomically add it into Y.
 // EPI_COMBINE: write it to partial plane z with device-coherent stores, then
 // arrive_and_combine.
 template <int BM, int BN, int THREADS, int CPS, int EPI, int FM, int FN>
@@ -247,6 +293,21 @@ __device__ __forceinline__ void finish_slice(const f32x4 (&acc)[FM][FN], const G
                                              int lane, int tid, int* s_last)
 {
     if (EPI == EPI_STORE) {
+        if (g.epi) {
+            // the final product of a single-slice addmm
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int row = wrow0 + fm * 16 + 4 * (lane >> 4) + q;
+                        const int col = wcol0 + fn * 16 + (lane & 15);
+                        if (row < g.M && col < g.N)
+                            write_final1(g, row, col, acc[fm][fn][q]);
+                    }
+            return;
+        }
         store_tile<FM, FN>(acc, g.Y + (size_t)tc.z * g.out_z_stride, g.ldy, g.M, g.N, wrow0,
                            wcol0, lane, false);
         return;

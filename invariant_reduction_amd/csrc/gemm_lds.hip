@@ -153,11 +153,12 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af
 // COHERENT: device-coherent (sc1) buffer stores, for partials that another
 // workgroup combines.  Needs STAGES * STAGE_BYTES >= 64 KiB.
 template <bool COHERENT>
-__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], float* out,
-                                                   int ld, int M, int N, int row0, int col0,
+__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
+                                                   float* out, int ld, int row0, int col0,
                                                    int wm, int wn, int lane, int tid,
                                                    uint8_t* smem)
 {
+    const int M = g.M, N = g.N;
     float* t = reinterpret_cast<float*>(smem);
     __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
@@ -171,12 +172,11 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], f
                 t[r * BN + (c ^ (16 * ((r >> 2) & 3)))] = acc[fm][fn][q];
             }
     __syncthreads();
-    // Stores go through a raw buffer based at the tile's first element; a
-    // piece outside M x N gets an offset past the record count, and the
-    // hardware drops it, so the loop has no branch and the reads above stay
-    // batched.
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        out + (size_t)row0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+    // Stores (and epilogue loads of C) go through raw buffers based at the
+    // tile's first element; a piece outside M x N gets an offset past the
+    // record count, and the hardware drops the store (a load returns
+    // zeros), so the loops have no branch and the reads above stay batched.
+    constexpr int OOB = (int)0x80000000u;
     // all of a thread's row pieces are read before the first store
     constexpr int ITER = BM * BN / 4 / THREADS;
     static_assert(ITER * THREADS * 4 == BM * BN, "whole float4 pieces per thread");
@@ -187,13 +187,59 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], f
         const int r = v / (BN / 4), c4 = v % (BN / 4);
         val[i] = *reinterpret_cast<const u32x4*>(t + r * BN + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
     }
+    if (COHERENT || !g.epi) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            out + (size_t)row0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int v = tid + i * THREADS;
+            const int r = v / (BN / 4), c4 = v % (BN / 4);
+            const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
+            const int off = in ? (r * ld + 4 * c4) * 4 : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, COHERENT ? CPOL_SC1 : 0);
+        }
+        return;
+    }
+    // the final product of a single-slice addmm: y = beta*C + alpha*p
+    __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(g.C ? g.C : g.Y) + (size_t)row0 * g.ldc + col0, 0, 0x7fffffff,
+        RAW_BUFFER_FLAGS);
+    void* ybase = g.out_bf16 ? (void*)(reinterpret_cast<uint16_t*>(g.Y) + (size_t)row0 * g.ldy + col0)
+                             : (void*)(g.Y + (size_t)row0 * g.ldy + col0);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(ybase, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+    u32x4 cv[ITER];
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
         const int v = tid + i * THREADS;
         const int r = v / (BN / 4), c4 = v % (BN / 4);
         const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
-        const int off = in ? (r * ld + 4 * c4) * 4 : (int)0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, COHERENT ? CPOL_SC1 : 0);
+        cv[i] = u32x4{0u, 0u, 0u, 0u};
+        if (g.C)
+            cv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rc, in ? (int)((r * g.ldc + 4 * c4) * 4) : OOB, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        const int v = tid + i * THREADS;
+        const int r = v / (BN / 4), c4 = v % (BN / 4);
+        const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = epi_value(g, __uint_as_float(val[i][e]), __uint_as_float(cv[i][e]));
+        if (g.out_bf16) {
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 o = {f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16),
+                             f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(o, ry, in ? (int)((r * g.ldy + 4 * c4) * 2) : OOB,
+                                                  0, 0);
+        } else {
+            const u32x4 o = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                             __float_as_uint(y[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(o, ry, in ? (int)((r * g.ldy + 4 * c4) * 4) : OOB,
+                                                   0, 0);
+        }
     }
 }
 
@@ -366,8 +412,8 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             out = g.part + (size_t)tc.z * g.M * g.N;
             ld = g.N;
         }
-        store_tile_via_lds<EPI == EPI_COMBINE>(acc, out, ld, g.M, g.N, row0, col0, wm, wn,
-                                               lane, tid, smem);
+        store_tile_via_lds<EPI == EPI_COMBINE>(acc, g, out, ld, row0, col0, wm, wn, lane, tid,
+                                               smem);
         if constexpr (EPI == EPI_COMBINE) {
             int* s_last = reinterpret_cast<int*>(smem + scratch_offset + SCRATCH_BYTES);
             arrive_and_combine<BM, BN, THREADS, CPS>(g, tc, tid, s_last);
@@ -430,8 +476,11 @@ bool lds_engine_supports(const GemmArgs& g, int cps)
         return false;
     const size_t xbytes = ((size_t)(lds::BM - 1) * g.ldx + g.K) * 2;
     const size_t wbytes = ((size_t)g.K * g.ldw) * 2;
-    // output rows of the tile (Y at ldy, or partial planes at N) likewise
-    const size_t ld = (size_t)(g.ldy > g.N ? g.ldy : g.N);
+    // output rows of the tile (Y at ldy, partial planes at N, C at ldc)
+    // likewise
+    size_t ld = (size_t)(g.ldy > g.N ? g.ldy : g.N);
+    if (g.epi && g.C && (size_t)g.ldc > ld)
+        ld = (size_t)g.ldc;
     const size_t ybytes = ((lds::BM - 1) * ld + lds::BN) * 4;
     return xbytes < 0x7fffffffu && wbytes < 0x7fffffffu && ybytes < 0x7fffffffu;
 }

@@ -23,6 +23,16 @@ struct GemmArgs {
     int Kc;               // chunk width
     int slices;           // grid slices along K
     int tiles_m, tiles_n;
+    // Output epilogue (the addmm entry point), applied only where the final
+    // value p of an element of Y is written, never to partials or shard
+    // roots: y = beta*C[row][col] + alpha*p (y = alpha*p when C is null),
+    // each product and the sum rounded as written; stored as bf16 (nearest
+    // even) when out_bf16, else fp32.  epi == 0: y = p as fp32.
+    int epi;
+    const float* C;
+    long ldc;             // 0: C is one row, broadcast to every row
+    float alpha, beta;
+    int out_bf16;
 };
 
 void tile_shape(int tile, int* bm, int* bn);
@@ -39,6 +49,10 @@ hipError_t launch_cast_bf16(const float* x, uint16_t* y, size_t n, hipStream_t s
 
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows,
                           int hidden, float eps, hipStream_t s);
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int rows,
+                               int hidden, float eps, hipStream_t s);
+// y = epilogue(p = 0) over an M x N output: the addmm of an empty product
+hipError_t launch_epilogue_only(const GemmArgs& g, hipStream_t s);
 hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s);
 hipError_t launch_mean(const float* x, float* y, int rows, int cols, hipStream_t s);
 

@@ -18,6 +18,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "bf16.h"
 #include "kernels.h"
 
 namespace detred {
@@ -56,9 +57,12 @@ __device__ __forceinline__ float block_sum(float v, float* red)
 // ------------------------------------------------------------------ RMSNorm
 constexpr int RMS_THREADS = 256;
 
+// OutT float: fp32 output; OutT uint16_t: the same fp32 values rounded to
+// bf16 (nearest even) as they are stored.
+template <class OutT>
 __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ gamma,
-                                                              float* __restrict__ y, int hidden,
+                                                              OutT* __restrict__ y, int hidden,
                                                               float eps)
 {
     __shared__ float red[RMS_THREADS / 64];
@@ -81,7 +85,6 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
     const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
 
     const uint4* gr = reinterpret_cast<const uint4*>(gamma);
-    float4* yr = reinterpret_cast<float4*>(y + row * hidden);
     for (int v = threadIdx.x; v < nv; v += RMS_THREADS) {
         const uint4 q = xr[v], gq = gr[v];
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -92,8 +95,18 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
             o[2 * i] = (bf16_lo(w[i]) * inv) * bf16_lo(gw[i]);
             o[2 * i + 1] = (bf16_hi(w[i]) * inv) * bf16_hi(gw[i]);
         }
-        yr[2 * v] = make_float4(o[0], o[1], o[2], o[3]);
-        yr[2 * v + 1] = make_float4(o[4], o[5], o[6], o[7]);
+        if constexpr (sizeof(OutT) == 4) {
+            float4* yr = reinterpret_cast<float4*>(y + row * hidden);
+            yr[2 * v] = make_float4(o[0], o[1], o[2], o[3]);
+            yr[2 * v + 1] = make_float4(o[4], o[5], o[6], o[7]);
+        } else {
+            uint4 b;
+            b.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+            b.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+            b.z = f32_to_bf16_bits(o[4]) | (f32_to_bf16_bits(o[5]) << 16);
+            b.w = f32_to_bf16_bits(o[6]) | (f32_to_bf16_bits(o[7]) << 16);
+            reinterpret_cast<uint4*>(y + row * hidden)[v] = b;
+        }
     }
 }
 
@@ -291,8 +304,16 @@ __global__ __launch_bounds__(ROW_THREADS) void mean_kernel(const float* __restri
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows,
                           int hidden, float eps, hipStream_t s)
 {
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(RMS_THREADS), 0, s, x, gamma, y, hidden,
-                       eps);
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(RMS_THREADS), 0, s, x, gamma, y,
+                       hidden, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int rows,
+                               int hidden, float eps, hipStream_t s)
+{
+    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(rows), dim3(RMS_THREADS), 0, s, x, gamma, y,
+                       hidden, eps);
     return hipGetLastError();
 }
 

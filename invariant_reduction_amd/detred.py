@@ -17,6 +17,7 @@ import torch
 from . import build as _build
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
 
 _lib = None
 
@@ -33,6 +34,11 @@ SIGNATURES = {
     "detred_gemm_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "detred_workspace_init": ([_P, _Z, _P], _I),
     "det_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "det_splitk_addmm": ([_P, _I, _P, _I, _P, _I, _F, _F, _P, _I, _I, _I, _I, _I, _I, _P, _Z,
+                          _P], _I),
+    "det_lora_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "det_lora_forward": ([_P, _I, _P, _I, _P, _I, _P, _I, _F, _P, _I, _I, _I, _I, _I, _P, _Z,
+                          _P], _I),
     "atomic_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "tree_tp_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "tree_tp_shards_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _P], _I),
@@ -40,6 +46,7 @@ SIGNATURES = {
     "tree_combine_f32": ([_P, _Z, _I, _P, _Z, _P], _I),
     "detred_f32_to_bf16": ([_P, _P, _Z, _P], _I),
     "inv_rmsnorm": ([_P, _P, _P, _I, _I, _F, _P], _I),
+    "inv_rmsnorm_bf16": ([_P, _P, _P, _I, _I, _F, _P], _I),
     "inv_log_softmax": ([_P, _P, _I, _I, _P], _I),
     "inv_mean": ([_P, _P, _I, _I, _P], _I),
 }
@@ -190,6 +197,64 @@ def det_splitk_gemm(X, W, Y, split_k=0, ws=None, stream=None):
 
 
 @_entry
+def det_splitk_addmm(X, W, Y, C=None, alpha=1.0, beta=1.0, split_k=0, ws=None, stream=None):
+    """Y = beta*C + alpha*(X W) with the canonical product; Y fp32 or bf16
+    (bf16/int16/uint16 dtype = bf16 output).  C: None, a length-N fp32 bias
+    (broadcast to every row) or an fp32 [M, N] matrix."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    out_bf16 = Y.dtype in _BF16_TYPES
+    py, ldy = _mat(Y, _BF16_TYPES + (torch.float32,), "Y")
+    M, N, K = _gemm_dims(X, W, Y)
+    if C is None:
+        pc, ldc = ctypes.c_void_p(None), 0
+    elif C.dim() == 1:
+        if C.dtype != torch.float32 or not C.is_cuda or not C.is_contiguous() or C.numel() != N:
+            raise ValueError("a bias C must be a contiguous fp32 GPU vector of length N")
+        pc, ldc = ctypes.c_void_p(C.data_ptr()), 0
+    else:
+        pc, ldc = _mat(C, (torch.float32,), "C")
+        if tuple(C.shape) != (M, N):
+            raise ValueError("C must be [M, N]")
+    pws, nws = _ws(ws)
+    return "det_splitk_addmm", (px, ldx, pw, ldw, pc, ldc, float(alpha), float(beta), py, ldy,
+                                  BF16 if out_bf16 else F32, M, N, K, split_k, pws, nws,
+                                  _stream(stream))
+
+
+def det_lora_workspace_bytes(M, N, K, r):
+    return int(lib().det_lora_workspace_bytes(M, N, K, r))
+
+
+def lora_workspace(M, N, K, r, device="cuda", stream=None):
+    """Allocate (through torch) and zero the det_lora_forward workspace."""
+    nbytes = det_lora_workspace_bytes(M, N, K, r)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
+    detred_workspace_init(ws, stream)
+    return ws
+
+
+@_entry
+def det_lora_forward(X, W, A, B, Y, scale, ws, stream=None):
+    """Y (bf16) = bf16(X W + scale * (bf16(X A) B)), every step in a fixed order."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    pa, lda = _mat(A, _BF16_TYPES, "A")
+    pb, ldb = _mat(B, _BF16_TYPES, "B")
+    py, ldy = _mat(Y, _BF16_TYPES, "Y")
+    M, K = X.shape
+    N, r = W.shape[1], A.shape[1]
+    if W.shape[0] != K or A.shape[0] != K or tuple(B.shape) != (r, N) or tuple(Y.shape) != (M, N):
+        raise ValueError("shape mismatch: X %s W %s A %s B %s Y %s" % (
+            tuple(X.shape), tuple(W.shape), tuple(A.shape), tuple(B.shape), tuple(Y.shape)))
+    pws, nws = _ws(ws)
+    return "det_lora_forward", (px, ldx, pw, ldw, pa, lda, pb, ldb, float(scale), py, ldy, M, N,
+                                  K, r, pws, nws, _stream(stream))
+
+
+@_entry
 def atomic_splitk_gemm(X, W, Y, split_k=0, stream=None):
     """The nondeterministic control: zero Y, then fp32 atomic slice adds."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
@@ -282,6 +347,19 @@ def inv_rmsnorm(x, gamma, y, eps, stream=None):
         raise ValueError("y must match x's shape")
     return "inv_rmsnorm", (px, ctypes.c_void_p(gamma.data_ptr()), py, rows, hidden,
                              float(eps), _stream(stream))
+
+
+@_entry
+def inv_rmsnorm_bf16(x, gamma, y, eps, stream=None):
+    """inv_rmsnorm with a bf16 output y[rows,hidden]."""
+    px, rows, hidden = _rows(x, _BF16_TYPES, "x")
+    py, r2, h2 = _rows(y, _BF16_TYPES, "y")
+    if gamma.dtype not in _BF16_TYPES or not gamma.is_cuda or not gamma.is_contiguous() or gamma.numel() != hidden:
+        raise TypeError("gamma must be a contiguous bf16 GPU vector of length hidden")
+    if (r2, h2) != (rows, hidden):
+        raise ValueError("y must match x's shape")
+    return "inv_rmsnorm_bf16", (px, ctypes.c_void_p(gamma.data_ptr()), py, rows, hidden,
+                                  float(eps), _stream(stream))
 
 
 @_entry

@@ -22,6 +22,8 @@ STREAM_W = 1
 STREAM_B = 2
 STREAM_GAMMA = 3
 STREAM_LOGITS = 4
+STREAM_BASE = 5
+STREAM_BIAS = 6
 
 
 def rng(seed, stream):
@@ -89,3 +91,18 @@ def rmsnorm_inputs(B, H, seed=0):
 def logits_inputs(B, V, seed=0):
     """log_softmax / mean: logits[B,V] ~ N(0,3), float32."""
     return normal_f32((B, V), 0.0, 3.0, seed, STREAM_LOGITS)
+
+
+def lora_layer_inputs(M, K, N, r, seed=0):
+    """A LoRA-adapted linear layer: X[M,K] ~ N(0,1), base W[K,N], A[K,r] and
+    B[r,N] ~ N(0,0.02), bf16 bits."""
+    X = normal_bf16((M, K), 0.0, 1.0, seed, STREAM_X)
+    W = normal_bf16((K, N), 0.0, 0.02, seed, STREAM_BASE)
+    A = normal_bf16((K, r), 0.0, 0.02, seed, STREAM_W)
+    B = normal_bf16((r, N), 0.0, 0.02, seed, STREAM_B)
+    return X, W, A, B
+
+
+def bias_inputs(N, seed=0):
+    """An fp32 bias row of N values ~ N(0,1)."""
+    return normal_f32((N,), 0.0, 1.0, seed, STREAM_BIAS)

@@ -88,6 +88,38 @@ def gemm(X, W, with_magnitude=True):
     return Y, A
 
 
+def addmm(X, W, C=None, alpha=1.0, beta=1.0):
+    """y = beta*C + alpha*(X W) in fp64: the addmm of the "Batch Invariant
+    Ops" project summary (Highlighted Details).  C is None, a length-N bias
+    added to every row, or an [M,N] array.  Returns (Y, A) with
+    A = |beta*C| + |alpha| * sum_k |x w|, the magnitude that scales the
+    tolerance of a binary32 result."""
+    P, Am = gemm(X, W)
+    if C is None:
+        Cm = np.zeros_like(P)
+    else:
+        Cm = np.asarray(C, dtype=np.float64)
+        if Cm.ndim == 1:
+            if Cm.shape[0] != P.shape[1]:
+                raise ValueError("a bias must have one value per output column")
+            Cm = np.broadcast_to(Cm[None, :], P.shape)
+        elif Cm.shape != P.shape:
+            raise ValueError("C must be [M, N]")
+    Y = beta * Cm + alpha * P
+    return Y, abs(beta) * np.abs(Cm) + abs(alpha) * Am
+
+
+def lora_forward(X, W, Zb, B, scale):
+    """The LoRA-adapted layer in fp64: Y = X W + scale * (Zb B), with Zb the
+    bf16 bits of the shrink output X A after its cast ("Reproducible LoRA
+    Inference Through Deterministic Split-K Reduction", Highlights and Q&A:
+    the base product plus the expand of the shrink).  Returns (Y, A) with
+    A = sum_k |x w| + |scale| * sum_l |z b|."""
+    Yb, Ab = gemm(X, W)
+    Ye, Ae = gemm(Zb, B)
+    return Yb + scale * Ye, Ab + abs(scale) * Ae
+
+
 def rmsnorm(x, gamma, eps):
     """RMSNorm rows in fp64 (oracle.c, oracle_rmsnorm_f64)."""
     x = _u16(x)

@@ -128,3 +128,45 @@ def test_other_entry_points_reject():
     assert L.inv_mean(A16, A16b, 4, 0, None) == detred.EUNSUPPORTED
     assert L.inv_mean(None, A16b, 4, 8, None) == detred.EINVAL
     assert L.detred_workspace_init(None, 16, None) == detred.EINVAL
+
+
+def test_addmm_lora_and_bf16_rmsnorm_reject():
+    L = detred.lib()
+    f = ctypes.c_float
+    # det_splitk_addmm(X, ldx, W, ldw, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K, S, ws, ws_bytes, s)
+    args = lambda **kw: [kw.get("X", A16), 512, A16b, 16, kw.get("C", A16c), kw.get("ldc", 16),
+                         f(1.0), f(1.0), kw.get("Y", A16), 16, kw.get("dt", detred.F32),
+                         16, 16, 512, kw.get("S", 1), None, 0, None]
+    assert L.det_splitk_addmm(*args(dt=2)) == detred.EINVAL
+    assert L.det_splitk_addmm(*args(C=MIS)) == detred.EINVAL
+    assert L.det_splitk_addmm(*args(ldc=8)) == detred.EINVAL      # ldc < N
+    assert L.det_splitk_addmm(*args(ldc=18)) == detred.EINVAL     # ldc % 4 != 0
+    assert L.det_splitk_addmm(*args(ldc=-4)) == detred.EINVAL
+    assert L.det_splitk_addmm(*args(X=MIS)) == detred.EINVAL
+    assert L.det_splitk_addmm(*args(S=3)) == detred.EUNSUPPORTED
+    assert L.det_splitk_addmm(*args(S=4)) == detred.EWORKSPACE
+    # M == 0 launches nothing
+    a = args()
+    a[11] = 0
+    assert L.det_splitk_addmm(*a) == detred.OK
+    # det_lora_forward(X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy, M, N, K, r, ws, ws_bytes, s)
+    WS = 0x100000                     # fake, 256-byte aligned
+    big = 1 << 40
+    lora = lambda **kw: [kw.get("X", A16), 512, A16b, 64, A16c, kw.get("r", 16), A16b,
+                         64, f(1.0), A16c, 64, 16, 64, 512, kw.get("r", 16),
+                         kw.get("ws", WS), kw.get("nws", big), None]
+    assert L.det_lora_forward(*lora(r=0)) == detred.EINVAL
+    assert L.det_lora_forward(*lora(r=12)) == detred.EUNSUPPORTED
+    assert L.det_lora_forward(*lora(ws=None)) == detred.EWORKSPACE
+    assert L.det_lora_forward(*lora(ws=WS + 16)) == detred.EWORKSPACE
+    assert L.det_lora_forward(*lora(nws=16)) == detred.EWORKSPACE
+    assert L.det_lora_forward(*lora(X=MIS)) == detred.EINVAL
+    assert L.det_lora_workspace_bytes(16, 64, 512, 0) == 0
+    need = L.det_lora_workspace_bytes(16, 64, 512, 16)
+    # base [16,64] + shrink fp32 [16,16] + its bf16 + the split-K workspaces of
+    # the base product and the shrink (both split 8 by the policy: N <= 64)
+    assert need == 4096 + 1024 + 512 + L.detred_gemm_workspace_bytes(16, 64, 512, 8) + \
+        L.detred_gemm_workspace_bytes(16, 16, 512, 8)
+    assert L.inv_rmsnorm_bf16(A16, A16b, A16c, 4, 4100, f(1e-6), None) == detred.EUNSUPPORTED
+    assert L.inv_rmsnorm_bf16(A16, None, A16c, 4, 4096, f(1e-6), None) == detred.EINVAL
+    assert L.inv_rmsnorm_bf16(A16, A16b, MIS, 4, 4096, f(1e-6), None) == detred.EINVAL

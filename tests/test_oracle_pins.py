@@ -131,6 +131,65 @@ def test_gemm_empty_k_is_zero():
     assert Y.shape == (3, 5) and np.all(Y == 0) and np.all(A == 0)
 
 
+# --- addmm and the LoRA layer ------------------------------------------------
+
+
+def test_addmm_integer_brute_force_and_bias_direction():
+    # integer inputs, dyadic alpha/beta: every value is exact in fp64, so the
+    # oracle must equal Python integer/Fraction arithmetic written out
+    # element by element; the bias has distinct values per column and
+    # M != N, so a bias added along the wrong axis fails
+    M, N, K = 5, 7, 12
+    X = inputs.integer_bf16((M, K), -8, 8, 21, 0)
+    W = inputs.integer_bf16((K, N), -8, 8, 21, 1)
+    xi = inputs.bf16_bits_to_f32(X).astype(np.int64)
+    wi = inputs.bf16_bits_to_f32(W).astype(np.int64)
+    bias = np.arange(N, dtype=np.float32) * 3 - 5
+    Cfull = (np.arange(M * N, dtype=np.float32).reshape(M, N) - 17) / 4
+    for C in (None, bias, Cfull):
+        for alpha, beta in ((1.0, 1.0), (0.5, -2.0), (-1.25, 0.75)):
+            Y, A = oracle.addmm(X, W, C, alpha, beta)
+            for i in range(M):
+                for j in range(N):
+                    p = sum(int(xi[i, k]) * int(wi[k, j]) for k in range(K))
+                    pa = sum(abs(int(xi[i, k]) * int(wi[k, j])) for k in range(K))
+                    c = 0 if C is None else (C[j] if C.ndim == 1 else C[i, j])
+                    want = Fraction(beta) * Fraction(float(c)) + Fraction(alpha) * p
+                    mag = abs(Fraction(beta) * Fraction(float(c))) + abs(Fraction(alpha)) * pa
+                    assert Fraction(Y[i, j]) == want, (i, j, alpha, beta)
+                    assert Fraction(A[i, j]) == mag, (i, j)
+
+
+def test_addmm_zero_weight_and_zero_alpha_give_scaled_c():
+    X, W = inputs.dense_inputs(4, 64, 6, seed=3)
+    C = np.linspace(-2, 3, 24, dtype=np.float32).reshape(4, 6)
+    Y, A = oracle.addmm(X, np.zeros_like(W), C, 0.7, -1.5)
+    np.testing.assert_array_equal(Y, -1.5 * C.astype(np.float64))
+    Y, A = oracle.addmm(X, W, C, 0.0, 2.0)
+    np.testing.assert_array_equal(Y, 2.0 * C.astype(np.float64))
+    np.testing.assert_array_equal(A, 2.0 * np.abs(C.astype(np.float64)))
+
+
+def test_lora_forward_integer_brute_force():
+    # Y = X W + scale * (Zb B) written out with Fractions on integer inputs
+    M, N, K, r = 3, 8, 16, 4
+    X = inputs.integer_bf16((M, K), -4, 4, 9, 0)
+    W = inputs.integer_bf16((K, N), -4, 4, 9, 1)
+    Z = inputs.integer_bf16((M, r), -4, 4, 9, 2)
+    B = inputs.integer_bf16((r, N), -4, 4, 9, 3)
+    f = lambda a: inputs.bf16_bits_to_f32(a).astype(np.int64)
+    xi, wi, zi, bi = f(X), f(W), f(Z), f(B)
+    Y, A = oracle.lora_forward(X, W, Z, B, -0.5)
+    for i in range(M):
+        for j in range(N):
+            base = sum(int(xi[i, k]) * int(wi[k, j]) for k in range(K))
+            exp = sum(int(zi[i, l]) * int(bi[l, j]) for l in range(r))
+            assert Fraction(Y[i, j]) == base + Fraction(-1, 2) * exp, (i, j)
+            mag = sum(abs(int(xi[i, k]) * int(wi[k, j])) for k in range(K)) + \
+                Fraction(1, 2) * sum(abs(int(zi[i, l]) * int(bi[l, j])) for l in range(r))
+            assert Fraction(A[i, j]) == mag, (i, j)
+
+
 # --- RMSNorm ------------------------------------------------------------------
 
 def test_rmsnorm_pm1_closed_form():
