@@ -88,8 +88,7 @@ class Workload:
         self.y_mean = torch.empty((B,), dtype=f32, device=dev)
         self.ws_shr = detred.workspace(B, R, H, 8, dev)
         self.p_tp = torch.empty((TP_T, TP_M, TP_N), dtype=f32, device=dev)
-        dsplit = detred.policy(F, H)["default_split"]
-        self.ws_dns = detred.workspace(B, F, H, dsplit, dev)
+        self.ws_dns = detred.workspace(B, F, H, 0, dev)
 
     def ops(self):
         """(name, launch, det-GEMM flops, algorithmic bytes) in step order.
@@ -224,7 +223,7 @@ def invariance(wl, dev):
     # dense: prefixes, split 4 vs policy
     for M in (1, 16, 128):
         y = torch.empty((M, F), dtype=f32, device=dev)
-        detred.det_splitk_gemm(wl.X[:M], wl.W, y, 0, None)
+        detred.det_splitk_gemm(wl.X[:M], wl.W, y, 0, detred.workspace(M, F, H, 0, dev))
         cmp(y, wl.y_dns[:M])
     y = torch.empty((B, F), dtype=f32, device=dev)
     detred.det_splitk_gemm(wl.X, wl.W, y, 4, detred.workspace(B, F, H, 4, dev))
@@ -264,6 +263,80 @@ def tp_breakdown(wl, dev, stream):
     y = torch.empty((TP_M, TP_N), dtype=torch.float32, device=dev)
     out["combine_T8_us"] = round(median_time_us(
         detred.prepare(detred.tree_combine_f32, P, y), 20, stream, warm=3)[0], 1)
+    return out
+
+
+def divergence(dev, stream):
+    """Replay divergence of det vs atomic split-K=8 over 100 replays on the
+    LoRA shrink shapes: the share of replays 1..99 that differ anywhere from
+    replay 0, the number of distinct outputs among the 100, and the mean
+    fraction of elements that differ from replay 0."""
+    out = {}
+    for (M, K, r) in [(16, 512, 16), (256, 4096, 64)]:
+        X, A, _ = inputs.lora_inputs(M, K, r, 0)
+        Xd, Ad = d16(X, dev), d16(A, dev)
+        Y = torch.empty((M, r), dtype=torch.float32, device=dev)
+        ws = detred.workspace(M, r, K, 8, dev)
+        res = {}
+        for name, fn in (("det8", detred.prepare(detred.det_splitk_gemm, Xd, Ad, Y, 8, ws)),
+                         ("atomic8", detred.prepare(detred.atomic_splitk_gemm, Xd, Ad, Y, 8))):
+            outs = []
+            for _ in range(100):
+                fn()
+                outs.append(Y.view(torch.int32).clone())
+            torch.cuda.synchronize()
+            ref = outs[0]
+            differ = [int((o != ref).sum()) for o in outs[1:]]
+            hashes = {hashlib.sha256(o.cpu().numpy().tobytes()).hexdigest() for o in outs}
+            res[name] = {"replays_differing_pct": round(100.0 * sum(d > 0 for d in differ) / 99, 2),
+                         "distinct_outputs": len(hashes),
+                         "mean_elements_differing_pct": round(100.0 * sum(differ) / 99 / ref.numel(), 3)}
+        out["%dx%dx%d" % (M, r, K)] = res
+    return out
+
+
+def extensions(dev, stream):
+    """The next-row operations, timed alone (median/p10/p90 of 50 launches):
+    the one-call LoRA layer (hidden 4096, rank 64, batch 256), addmm with a
+    bias row into a bf16 output on the dense shape, and bf16 RMSNorm."""
+    out = {}
+    gb = 2
+
+    def record(name, fn, flops, nbytes):
+        med, p10, p90 = median_time_us(fn, 50, stream, warm=5)
+        st = {"median_us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+              "gbs": round(nbytes / (med * 1e-6) / 1e9, 1)}
+        if flops:
+            st["tflops"] = round(flops / (med * 1e-6) / 1e12, 2)
+        if flops and flops / nbytes >= RIDGE:
+            st["roofline"] = {"bound": "mfma", "frac": round(flops / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        else:
+            st["roofline"] = {"bound": "hbm", "frac": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        st["algorithmic_bytes"] = nbytes
+        out[name] = st
+
+    X, W, A, Bm = inputs.lora_layer_inputs(B, H, H, R, 0)
+    Xd, Wd, Ad, Bd = (d16(t, dev) for t in (X, W, A, Bm))
+    Y = torch.empty((B, H), dtype=torch.int16, device=dev)
+    ws = detred.lora_workspace(B, H, H, R, dev)
+    record("lora_layer_%dx%dx%d_r%d" % (B, H, H, R),
+           detred.prepare(detred.det_lora_forward, Xd, Wd, Ad, Bd, Y, 2.0, ws),
+           2 * B * H * H + 2 * B * H * R + 2 * B * R * H,
+           B * H * gb + H * H * gb + H * R * gb + R * H * gb + B * H * gb)
+    _, Wdn = inputs.dense_inputs(B, H, F, 0)
+    Wdd = d16(Wdn, dev)
+    Xdd = d16(inputs.dense_inputs(B, H, F, 0)[0], dev)
+    bias = torch.from_numpy(inputs.bias_inputs(F, 0)).to(dev)
+    Yb = torch.empty((B, F), dtype=torch.int16, device=dev)
+    record("addmm_bias_bf16_%dx%dx%d" % (B, F, H),
+           detred.prepare(detred.det_splitk_addmm, Xdd, Wdd, Yb, bias, 1.0, 1.0, 0,
+                          detred.workspace(B, F, H, 0, dev)),
+           2 * B * H * F, B * H * gb + H * F * gb + F * 4 + B * F * gb)
+    x, g = inputs.rmsnorm_inputs(B, H, 0)
+    yr = torch.empty((B, H), dtype=torch.int16, device=dev)
+    record("rmsnorm_bf16_%dx%d" % (B, H),
+           detred.prepare(detred.inv_rmsnorm_bf16, d16(x, dev), d16(g, dev), yr, 1e-6),
+           0, B * H * gb + H * gb + B * H * gb)
     return out
 
 
@@ -368,7 +441,10 @@ def main():
     op_stats = {}
     for (name, _, fl, by), ts in zip(ops, per_op):
         avg = sum(ts) / len(ts)
-        st = {"avg_us": round(avg * 1000, 2), "median_us": round(statistics.median(ts) * 1000, 2)}
+        srt = sorted(ts)
+        st = {"avg_us": round(avg * 1000, 2), "median_us": round(statistics.median(ts) * 1000, 2),
+              "p10_us": round(srt[len(srt) // 10] * 1000, 2),
+              "p90_us": round(srt[(9 * len(srt)) // 10] * 1000, 2)}
         if fl:
             st["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
         st["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
@@ -386,13 +462,16 @@ def main():
     roof["traffic"] = measured_traffic(dname)
     roof["kernel"] = dname
 
-    ratios = tp = None
+    ratios = tp = div = ext = None
     same = total = 0
     if not args.quick:
         print("bench: latency ratios, invariance, tree-TP breakdown", file=sys.stderr, flush=True)
         ratios = latency_ratios(dev, stream)
         same, total = invariance(wl, dev)
         tp = tp_breakdown(wl, dev, stream)
+        div = divergence(dev, stream)
+        print("bench: next-row operations", file=sys.stderr, flush=True)
+        ext = extensions(dev, stream)
 
     # replays: every deterministic output is reproduced bit for bit; the
     # atomic control is counted
@@ -434,6 +513,8 @@ def main():
         "cpu_baseline": cpu,
         "ops": op_stats,
         "det_vs_atomic": ratios,
+        "replay_divergence": div,
+        "extensions": ext,
         "tree_tp_breakdown": tp,
         "bit_invariant_rows_pct": round(100.0 * same / max(total, 1), 4),
         "bit_invariant_rows_checked": total,

@@ -92,18 +92,30 @@ int detred_version(void);
  * length K (it never depends on M).  Writes, where the pointer is non-NULL:
  *   chunks   = P (1 or 8) and chunk_k = Kc;
  *   tile_m, tile_n = the workgroup output tile;
- *   default_split  = the split used when split_k = 0 is passed.
+ *   default_split  = the split split_k = 0 picks once M is large enough to
+ *                    give every CU an output tile (detred_auto_split).
  * Returns EINVAL for N < 0 or K < 0.
  */
 int detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
                   int *tile_n, int *default_split);
 
 /*
+ * The split that split_k = 0 selects for an M x N x K product.  The split
+ * only decides how many workgroups share the chunk tree; the bits of the
+ * result never depend on it (nor on M).  Outputs of at most 64 columns use
+ * one slice per chunk (S = P).  Wider ones use S = 1 when their tiles
+ * already cover at least 192 CUs, else the smallest S (<= P) with
+ * tiles*S >= 256.  Returns 0 for invalid arguments.
+ */
+int detred_auto_split(int M, int N, int K);
+
+/*
  * Workspace size in bytes that det_splitk_gemm (split_k = S) or tree_tp_gemm
  * (tp_shards = S) needs for an M x N output with reduction length K:
  * S fp32 partial arrays of M*N elements plus one 32-bit counter per output
- * tile, rounded up to 256 bytes.  0 when S == 1 (no workspace is used).
- * Returns 0 for invalid arguments as well.
+ * tile, rounded up to 256 bytes.  S = 0 means detred_auto_split(M, N, K).
+ * 0 when S == 1 (no workspace is used).  Returns 0 for invalid arguments as
+ * well.
  */
 size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards);
 
@@ -118,8 +130,8 @@ int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
 /*
  * Deterministic split-K product Y[M,N] (fp32) = X[M,K] W[K,N] (bf16), the
  * fixed-order split-K of the split-K paper (Highlights, Q&A) with the
- * canonical tree above.  split_k = S in {1,2,4,8} (S <= P), or 0 for the
- * policy's default.  With S > 1 each slice writes its fp32 partial into the
+ * canonical tree above.  split_k = S in {1,2,4,8} (S <= P), or 0 for
+ * detred_auto_split(M, N, K).  With S > 1 each slice writes its fp32 partial into the
  * workspace as S row-major [M][N] arrays (ld N) at byte offset 0, the last
  * slice of every output tile to finish adds the S partials in the fixed tree
  * order and writes Y; one launch in total.  ws may be NULL when S == 1.
@@ -190,7 +202,7 @@ int det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * but Y is zero-filled on the stream and every slice adds its partial into Y
  * with fp32 atomic additions, so the summation order follows the order in
  * which slices finish (split-K paper, Q&A: partial results combined with
- * floating-point atomic additions).  split_k as above (0 = default).  The
+ * floating-point atomic additions).  split_k as above (0 = automatic).  The
  * zero fill is part of the call.  Results agree with the oracle to the same
  * tolerance but are not bit-reproducible.
  */

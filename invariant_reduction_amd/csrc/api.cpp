@@ -109,11 +109,31 @@ GemmArgs make_args(const Policy& p, const uint16_t* X, int ldx, const uint16_t* 
     return g;
 }
 
-// Resolve split_k / tp_shards against the policy; 0 means the default.
-int resolve_split(const Policy& p, int split, int* out)
+// The split for split_k = 0.  The split only decides how many workgroups
+// share the chunk tree, never the bits.  Narrow outputs keep the policy's
+// split (one slice per chunk).  A wide product splits while its output tiles
+// leave CUs idle: S = 1 once the tiles cover 192 CUs (there the extra
+// partial traffic costs more than the idle CUs), else the smallest S with
+// tiles*S >= 256.  Chosen from timings of 1..1024-row products with
+// N in {1024, 4096, 14336} and K in {4096, 8192} on MI355X.
+int auto_split(const Policy& p, int M, int N)
+{
+    if (p.tile != TILE_L128)
+        return p.default_split;
+    const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+    if (tiles >= 192)
+        return 1;
+    int S = 1;
+    while (S < p.P && tiles * S < 256)
+        S *= 2;
+    return S;
+}
+
+// Resolve split_k / tp_shards against the policy; 0 means auto_split.
+int resolve_split(const Policy& p, int split, int M, int N, int* out)
 {
     if (split == 0)
-        split = p.default_split;
+        split = auto_split(p, M, N);
     if (!pow2_le8(split) || split > p.P)
         return DETRED_EUNSUPPORTED;
     *out = split;
@@ -152,13 +172,22 @@ int detred_policy(int N, int K, int* chunks, int* chunk_k, int* tile_m, int* til
     return DETRED_OK;
 }
 
+int detred_auto_split(int M, int N, int K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return 0;
+    return auto_split(policy_for(N, K), M, N);
+}
+
 size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards)
 {
-    if (M < 0 || N < 0 || K < 0 || !pow2_le8(split_or_shards))
-        return 0;
-    if (split_or_shards == 1)
+    if (M < 0 || N < 0 || K < 0)
         return 0;
     const Policy p = policy_for(N, K);
+    if (split_or_shards == 0)
+        split_or_shards = auto_split(p, M, N);
+    if (!pow2_le8(split_or_shards) || split_or_shards == 1)
+        return 0;
     return partial_bytes(M, N, split_or_shards) + counter_bytes(p, M, N);
 }
 
@@ -227,8 +256,8 @@ struct LoraLayout {
 LoraLayout lora_layout(int M, int N, int K, int r)
 {
     LoraLayout l;
-    l.s_base = policy_for(N, K).default_split;
-    l.s_z = policy_for(r, K).default_split;
+    l.s_base = auto_split(policy_for(N, K), M, N);
+    l.s_z = auto_split(policy_for(r, K), M, r);
     l.ws_base_bytes = detred_gemm_workspace_bytes(M, N, K, l.s_base);
     l.ws_z_bytes = detred_gemm_workspace_bytes(M, r, K, l.s_z);
     l.base = 0;
@@ -252,7 +281,7 @@ int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, floa
         return st;
     const Policy p = policy_for(N, K);
     int S = 0;
-    if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
+    if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
         return st;
     const GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
     return run_det(p, g, S, ws, ws_bytes, (hipStream_t)s);
@@ -270,7 +299,7 @@ int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
         return st;
     const Policy p = policy_for(N, K);
     int S = 0;
-    if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
+    if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
         return st;
     GemmArgs g = make_args(p, X, ldx, W, ldw, (float*)Y, ldy, M, N, K, S);
     g.epi = 1;
@@ -342,7 +371,7 @@ int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, f
         return st;
     const Policy p = policy_for(N, K);
     int S = 0;
-    if ((st = resolve_split(p, split_k, &S)) != DETRED_OK)
+    if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
         return st;
     hipStream_t hs = (hipStream_t)s;
     hipError_t e = launch_fill_zero(Y, ldy, M, N, hs);

@@ -31,6 +31,7 @@ SIGNATURES = {
     "detred_status_string": ([_I], ctypes.c_char_p),
     "detred_version": ([], _I),
     "detred_policy": ([_I, _I, _P, _P, _P, _P, _P], _I),
+    "detred_auto_split": ([_I, _I, _I], _I),
     "detred_gemm_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "detred_workspace_init": ([_P, _Z, _P], _I),
     "det_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
@@ -148,6 +149,14 @@ def policy(N, K):
 detred_policy = policy
 
 
+def detred_auto_split(M, N, K):
+    """The split that split_k = 0 selects (it never changes the bits)."""
+    return int(lib().detred_auto_split(M, N, K))
+
+
+auto_split = detred_auto_split
+
+
 def detred_gemm_workspace_bytes(M, N, K, split_or_shards):
     return int(lib().detred_gemm_workspace_bytes(M, N, K, split_or_shards))
 
@@ -159,7 +168,8 @@ def detred_workspace_init(ws, stream=None):
 
 def workspace(M, N, K, split_or_shards, device="cuda", stream=None):
     """Allocate (through torch) and zero a workspace for an M x N x K
-    product with the given split or shard count; None when none is needed."""
+    product with the given split or shard count (0: the automatic split);
+    None when none is needed."""
     nbytes = detred_gemm_workspace_bytes(M, N, K, split_or_shards)
     if nbytes == 0:
         return None

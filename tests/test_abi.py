@@ -55,6 +55,22 @@ def test_policy_is_locked_by_n_and_k():
     assert detred.lib().detred_policy(-1, 4, None, None, None, None, None) == detred.EINVAL
 
 
+def test_auto_split():
+    # wide outputs split while their 128 x 128 tiles leave CUs idle
+    assert detred.auto_split(256, 14336, 4096) == 1      # 224 tiles
+    assert detred.auto_split(1, 14336, 4096) == 4        # 112 tiles
+    assert detred.auto_split(256, 4096, 4096) == 4       # 64 tiles
+    assert detred.auto_split(512, 4096, 4096) == 2       # 128 tiles
+    assert detred.auto_split(1, 1024, 4096) == 8         # 8 tiles, capped at P
+    assert detred.auto_split(1024, 4096, 4096) == 1      # 256 tiles
+    assert detred.auto_split(1, 4096, 64) == 1           # one chunk
+    assert detred.auto_split(4096, 64, 4096) == 8        # narrow: one slice per chunk
+    assert detred.auto_split(-1, 64, 4096) == 0
+    assert detred.detred_gemm_workspace_bytes(256, 4096, 4096, 0) == \
+        detred.detred_gemm_workspace_bytes(256, 4096, 4096, 4)
+    assert detred.detred_gemm_workspace_bytes(256, 14336, 4096, 0) == 0
+
+
 def test_workspace_bytes():
     assert detred.detred_gemm_workspace_bytes(16, 16, 512, 1) == 0
     n = detred.detred_gemm_workspace_bytes(16, 16, 512, 8)

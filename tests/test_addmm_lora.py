@@ -41,8 +41,7 @@ def addmm(Xd, Wd, C, alpha, beta, S, dev, out=torch.float32):
     K = Xd.shape[1]
     Y = torch.full((M, N), -1, dtype=torch.int16, device=dev) if out != torch.float32 else \
         torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
-    Sx = S if S else detred.policy(N, K)["default_split"]
-    ws = detred.workspace(M, N, K, Sx, dev)
+    ws = detred.workspace(M, N, K, S, dev)
     detred.det_splitk_addmm(Xd, Wd, Y, C, alpha, beta, S, ws)
     return Y
 
@@ -191,9 +190,9 @@ def test_lora_forward_steps_and_parity(M, N, K, r, scale, dev):
     detred.det_lora_forward(Xd, Wd, Ad, Bd, Y, scale, detred.lora_workspace(M, N, K, r, dev))
     # the four steps one by one
     base = torch.empty((M, N), dtype=torch.float32, device=dev)
-    detred.det_splitk_gemm(Xd, Wd, base, 0, detred.workspace(M, N, K, detred.policy(N, K)["default_split"], dev))
+    detred.det_splitk_gemm(Xd, Wd, base, 0, detred.workspace(M, N, K, 0, dev))
     z = torch.empty((M, r), dtype=torch.float32, device=dev)
-    detred.det_splitk_gemm(Xd, Ad, z, 0, detred.workspace(M, r, K, detred.policy(r, K)["default_split"], dev))
+    detred.det_splitk_gemm(Xd, Ad, z, 0, detred.workspace(M, r, K, 0, dev))
     zb = torch.empty((M, r), dtype=torch.int16, device=dev)
     detred.detred_f32_to_bf16(z, zb)
     Yf = torch.empty((M, N), dtype=torch.float32, device=dev)

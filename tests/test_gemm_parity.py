@@ -19,7 +19,7 @@ def run_det(X, W, S, dev):
     M, K = X.shape
     N = W.shape[1]
     Y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
-    ws = detred.workspace(M, N, K, S if S else detred.policy(N, K)["default_split"], dev)
+    ws = detred.workspace(M, N, K, S, dev)
     detred.det_splitk_gemm(X, W, Y, S, ws)
     return Y, ws
 

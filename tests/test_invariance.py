@@ -18,7 +18,7 @@ def det(Xd, Wd, S, dev, M=None):
     M = Xd.shape[0] if M is None else M
     N, K = Wd.shape[1], Wd.shape[0]
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ws = detred.workspace(M, N, K, S if S else detred.policy(N, K)["default_split"], dev)
+    ws = detred.workspace(M, N, K, S, dev)
     detred.det_splitk_gemm(Xd[:M], Wd, Y, S, ws)
     return Y
 
@@ -63,7 +63,7 @@ def test_dense_rows_invariant_across_m(dev):
     ref = det(Xd, Wd, 0, dev)
     Y = torch.empty_like(ref)
     for M in DENSE_M:
-        detred.det_splitk_gemm(Xd[:M], Wd, Y[:M], 0, None)
+        detred.det_splitk_gemm(Xd[:M], Wd, Y[:M], 0, detred.workspace(M, 14336, 4096, 0, dev))
         torch.cuda.synchronize()
         assert torch.equal(Y[:M].view(torch.int32), ref[:M].view(torch.int32)), "M=%d" % M
 
