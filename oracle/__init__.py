@@ -50,6 +50,11 @@ def lib():
     L.oracle_fold_sum_f32.restype = ctypes.c_float
     L.oracle_f32_to_bf16_rne.argtypes = [_f32p, _u16p, ctypes.c_size_t]
     L.oracle_f32_to_bf16_rne.restype = None
+    L.oracle_decode_attention_f64.argtypes = [_u16p, _u16p, _u16p, ctypes.c_long, ctypes.c_long,
+                                              ctypes.c_long, np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS"),
+                                              _f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    L.oracle_decode_attention_f64.restype = None
     L.oracle_num_threads.argtypes = []
     L.oracle_num_threads.restype = ctypes.c_int
     _lib = L
@@ -118,6 +123,36 @@ def lora_forward(X, W, Zb, B, scale):
     Yb, Ab = gemm(X, W)
     Ye, Ae = gemm(Zb, B)
     return Yb + scale * Ye, Ab + abs(scale) * Ae
+
+
+def decode_attention(q, k, v, lens, scale, layout="bhtd"):
+    """Decode attention in fp64 (oracle.c, oracle_decode_attention_f64):
+    out[b][hq] = softmax_t(scale * q[b][hq] . k[b][hq // G][t]) weighted sum
+    of v[b][hq // G][t] over t < lens[b].  q: [B,Hq,D] uint16 bf16 bits;
+    k, v: uint16 [B,Hkv,L,D] (layout "bhtd") or [B,L,Hkv,D] ("bthd").
+    Returns (out, A, S): out and A = sum_t w_t |v_td| / sum_t w_t as
+    [B,Hq,D] fp64, and S = max_t |scale| * sum_d |q_d k_td| as [B,Hq]."""
+    q = _u16(q)
+    k = _u16(k)
+    v = _u16(v)
+    B, Hq, D = q.shape
+    if layout == "bhtd":
+        _, Hkv, L, _ = k.shape
+        sb, sh, st = Hkv * L * D, L * D, D
+    else:
+        _, L, Hkv, _ = k.shape
+        sb, sh, st = L * Hkv * D, D, Hkv * D
+    if k.shape != v.shape or Hq % Hkv:
+        raise ValueError("k and v must match and Hq must be a multiple of Hkv")
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    lens = np.minimum(lens, L).astype(np.int32)
+    out = np.empty((B, Hq, D), np.float64)
+    A = np.empty((B, Hq, D), np.float64)
+    S = np.empty((B, Hq), np.float64)
+    lib().oracle_decode_attention_f64(q.reshape(-1), k.reshape(-1), v.reshape(-1), sb, sh, st,
+                                      lens, out.reshape(-1), A.reshape(-1), S.reshape(-1),
+                                      B, Hq, Hkv, D, float(scale))
+    return out, A, S
 
 
 def rmsnorm(x, gamma, eps):

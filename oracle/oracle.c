@@ -23,6 +23,9 @@
  *    as reductions whose per-row result must not depend on batch size.
  *  - "Batch Invariant Ops" project summary (Highlighted Details): the
  *    supported operations mm, addmm, log_softmax and mean.
+ *  - "Restoring AI Reproducibility..." (2-3, 3-2): attention is a reduction
+ *    over the KV cache whose result must not depend on how it is split;
+ *    the decode-attention oracle is the softmax-weighted sum itself.
  *
  * Pins (see tests/test_oracle_pins.py): exact rational brute force on tiny
  * shapes, integer-valued inputs with exact integer results, closed forms for
@@ -33,6 +36,7 @@
 #include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* A bf16 value is the upper half of an IEEE binary32 value, so widening it
@@ -240,4 +244,70 @@ int oracle_num_threads(void)
         n = omp_get_num_threads();
     }
     return n;
+}
+
+/*
+ * Decode attention, one new query token per sequence ("Restoring AI
+ * Reproducibility...", 2-3 and 3-2: attention over the KV cache).  For
+ * sequence b and query head hq (KV head h = hq / G, G = Hq / Hkv):
+ *   sigma_t = scale * sum_d q[b][hq][d] * k[b][h][t][d],   t < len_b
+ *   w_t     = exp(sigma_t - max_t sigma_t)
+ *   out[d]  = sum_t w_t v[b][h][t][d] / sum_t w_t
+ * all in fp64.  Also, per output element, A = sum_t w_t |v_td| / sum_t w_t
+ * (the magnitude the tolerance scales with) and, per (b, hq),
+ * S = max_t scale * sum_d |q_d k_td| (the score magnitude).  q is [B][Hq][D]
+ * bf16; k and v are bf16 with D contiguous and strides (in elements)
+ * sb, sh, st for sequence, KV head and position.  len_b <= 0 gives zeros.
+ */
+void oracle_decode_attention_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 long sb, long sh, long st, const int *lens, double *out,
+                                 double *amag, double *smag, int B, int Hq, int Hkv, int D,
+                                 double scale)
+{
+    const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * Hq; ++bh) {
+        const int b = bh / Hq, hq = bh % Hq, h = hq / G;
+        const int len = lens[b];
+        double *o = out + (size_t)bh * D, *a = amag + (size_t)bh * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = a[d] = 0.0;
+        smag[bh] = 0.0;
+        if (len <= 0)
+            continue;
+        const uint16_t *qv = q + (size_t)bh * D;
+        double *sig = (double *)malloc(sizeof(double) * (size_t)len);
+        double mx = -INFINITY, smax = 0.0;
+        for (int t = 0; t < len; ++t) {
+            const uint16_t *kt = k + b * sb + h * sh + t * st;
+            double acc = 0.0, accabs = 0.0;
+            for (int d = 0; d < D; ++d) {
+                const double p = bf16_bits_to_f64(qv[d]) * bf16_bits_to_f64(kt[d]);
+                acc += p;
+                accabs += fabs(p);
+            }
+            sig[t] = scale * acc;
+            if (sig[t] > mx)
+                mx = sig[t];
+            if (fabs(scale) * accabs > smax)
+                smax = fabs(scale) * accabs;
+        }
+        double l = 0.0;
+        for (int t = 0; t < len; ++t) {
+            const double w = exp(sig[t] - mx);
+            l += w;
+            const uint16_t *vt = v + b * sb + h * sh + t * st;
+            for (int d = 0; d < D; ++d) {
+                const double x = bf16_bits_to_f64(vt[d]);
+                o[d] += w * x;
+                a[d] += w * fabs(x);
+            }
+        }
+        for (int d = 0; d < D; ++d) {
+            o[d] /= l;
+            a[d] /= l;
+        }
+        smag[bh] = smax;
+        free(sig);
+    }
 }

@@ -190,6 +190,88 @@ def test_lora_forward_integer_brute_force():
             assert Fraction(A[i, j]) == mag, (i, j)
 
 
+# --- decode attention -----------------------------------------------------------
+
+
+def test_decode_attention_brute_force_python():
+    # exact dot products (Fractions of the bf16 values), softmax with
+    # math.exp, written out per element: a different code path entirely
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, D, L = 2, 4, 2, 8, 6
+    q = rand_bf16((B, Hq, D), rng)
+    k = rand_bf16((B, Hkv, L, D), rng)
+    v = rand_bf16((B, Hkv, L, D), rng)
+    lens = [4, 6]
+    scale = 0.3
+    out, A, S = oracle.decode_attention(q, k, v, lens, scale)
+    G = Hq // Hkv
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            sig = [scale * float(sum(bf16_fraction(q[b, hq, d]) * bf16_fraction(k[b, h, t, d])
+                                     for d in range(D))) for t in range(lens[b])]
+            m = max(sig)
+            w = [math.exp(x - m) for x in sig]
+            l = sum(w)
+            for d in range(D):
+                want = sum(w[t] * float(bf16_fraction(v[b, h, t, d])) for t in range(lens[b])) / l
+                assert abs(out[b, hq, d] - want) <= 1e-12 * (1 + abs(want))
+                mag = sum(w[t] * abs(float(bf16_fraction(v[b, h, t, d]))) for t in range(lens[b])) / l
+                assert abs(A[b, hq, d] - mag) <= 1e-12 * (1 + mag)
+            smax = max(abs(scale) * float(sum(abs(bf16_fraction(q[b, hq, d]) * bf16_fraction(k[b, h, t, d]))
+                                              for d in range(D))) for t in range(lens[b]))
+            assert abs(S[b, hq] - smax) <= 1e-12 * smax
+
+
+def test_decode_attention_closed_forms_and_gqa_mapping():
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, D, L = 2, 6, 3, 16, 40
+    k = rand_bf16((B, Hkv, L, D), rng)
+    v = rand_bf16((B, Hkv, L, D), rng)
+    vf = inputs.bf16_bits_to_f32(v).astype(np.float64)
+    # q = 0: every score is 0, the weights are uniform and the output is the
+    # mean of the first len value rows of the query head's KV head
+    q0 = np.zeros((B, Hq, D), np.uint16)
+    lens = [17, 40]
+    out, _, _ = oracle.decode_attention(q0, k, v, lens, 0.25)
+    for b in range(B):
+        for hq in range(Hq):
+            np.testing.assert_allclose(out[b, hq], vf[b, hq // 2, :lens[b]].mean(axis=0), rtol=1e-12, atol=1e-14)
+    # one position: the output is that value row, exactly
+    q = rand_bf16((B, Hq, D), rng)
+    out, _, _ = oracle.decode_attention(q, k, v, [1, 1], 0.25)
+    for b in range(B):
+        for hq in range(Hq):
+            np.testing.assert_array_equal(out[b, hq], vf[b, hq // 2, 0])
+    # a length past the cache is clamped; a non-positive length gives zeros
+    o1, _, _ = oracle.decode_attention(q, k, v, [L + 5, 0], 0.25)
+    o2, _, _ = oracle.decode_attention(q, k, v, [L, 0], 0.25)
+    np.testing.assert_array_equal(o1, o2)
+    assert np.all(o1[1] == 0)
+
+
+def test_decode_attention_layouts_and_torch_fp64():
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, D, L = 3, 8, 2, 32, 50
+    q = rand_bf16((B, Hq, D), rng)
+    k = rand_bf16((B, Hkv, L, D), rng)
+    v = rand_bf16((B, Hkv, L, D), rng)
+    lens = [50, 7, 31]
+    out, _, _ = oracle.decode_attention(q, k, v, lens, 0.177)
+    kt = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+    vt = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    out2, _, _ = oracle.decode_attention(q, kt, vt, lens, 0.177, layout="bthd")
+    np.testing.assert_array_equal(out, out2)
+    f = lambda a: torch.from_numpy(inputs.bf16_bits_to_f32(a).astype(np.float64))
+    qf, kf, vf = f(q), f(k), f(v)
+    for b in range(B):
+        kk = kf[b].repeat_interleave(Hq // Hkv, dim=0)[:, :lens[b]]      # [Hq, len, D]
+        vv = vf[b].repeat_interleave(Hq // Hkv, dim=0)[:, :lens[b]]
+        w = torch.softmax(0.177 * torch.einsum("hd,htd->ht", qf[b], kk), dim=-1)
+        ref = torch.einsum("ht,htd->hd", w, vv).numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-13)
+
+
 # --- RMSNorm ------------------------------------------------------------------
 
 def test_rmsnorm_pm1_closed_form():
