@@ -298,7 +298,8 @@ def divergence(dev, stream):
 def extensions(dev, stream):
     """The next-row operations, timed alone (median/p10/p90 of 50 launches):
     the one-call LoRA layer (hidden 4096, rank 64, batch 256), addmm with a
-    bias row into a bf16 output on the dense shape, and bf16 RMSNorm."""
+    bias row into a bf16 output on the dense shape, decode attention with
+    the fixed 256-position KV split, and bf16 RMSNorm."""
     out = {}
     gb = 2
 
@@ -332,6 +333,22 @@ def extensions(dev, stream):
            detred.prepare(detred.det_splitk_addmm, Xdd, Wdd, Yb, bias, 1.0, 1.0, 0,
                           detred.workspace(B, F, H, 0, dev)),
            2 * B * H * F, B * H * gb + H * F * gb + F * 4 + B * F * gb)
+    # decode attention: 8B-class GQA (32 query heads, 8 KV heads, head dim
+    # 128), 64 sequences of 4096 cached positions; the 1 GiB cache is drawn
+    # on the device from a seeded generator
+    AB, AHq, AHkv, AD, AL = 64, 32, 8, 128, 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    qa = torch.randn((AB, AHq, AD), device=dev, generator=gen).to(torch.bfloat16)
+    ka = torch.randn((AB, AHkv, AL, AD), device=dev, generator=gen).to(torch.bfloat16)
+    va = torch.randn((AB, AHkv, AL, AD), device=dev, generator=gen).to(torch.bfloat16)
+    la = torch.full((AB,), AL, dtype=torch.int32, device=dev)
+    oa = torch.empty((AB, AHq, AD), dtype=torch.float32, device=dev)
+    wsa = detred.attention_workspace(AB, AHq, AD, AL, dev)
+    record("decode_attention_b%d_hq%d_hkv%d_d%d_len%d" % (AB, AHq, AHkv, AD, AL),
+           detred.prepare(detred.inv_decode_attention, qa, ka, va, la, oa, AD ** -0.5, wsa),
+           4 * AB * AHq * AL * AD, 2 * AB * AHkv * AL * AD * gb + AB * AHq * AD * (gb + 4))
+    del qa, ka, va
     x, g = inputs.rmsnorm_inputs(B, H, 0)
     yr = torch.empty((B, H), dtype=torch.int16, device=dev)
     record("rmsnorm_bf16_%dx%d" % (B, H),

@@ -306,6 +306,44 @@ int inv_log_softmax(const float *x, float *y, int rows, int cols,
  */
 int inv_mean(const float *x, float *y, int rows, int cols, detred_stream s);
 
+/*
+ * Workspace of inv_decode_attention: the per-chunk results of B*Hq query
+ * rows over ceil(max_len/256) chunks (D + 2 floats each), 256-byte aligned
+ * sections.  0 for invalid arguments.
+ */
+size_t inv_decode_attention_workspace_bytes(int B, int Hq, int D, int max_len);
+
+/*
+ * Batch-invariant decode attention: one new query token per sequence
+ * attends to its KV cache, with the reduction over positions split into
+ * chunks of a fixed size, 256 positions, whatever the batch ("Restoring AI
+ * Reproducibility: Thinking Machines Lab's Challenge to Overcome
+ * Nondeterminism", 2-3 and 3-2: attention needs a fixed-size split of the
+ * KV cache to keep its order independent of the batch).  For sequence b and
+ * query head hq (KV head h = hq / G, G = Hq / Hkv):
+ *   out[b][hq][:] = sum_t softmax_t(scale * q[b][hq] . k[b][h][t]) v[b][h][t]
+ * over t < min(lens[b], max_len) (zeros when that is <= 0).  Order: within
+ * a chunk of 256 positions, scores from 8-term fused multiply-add chains
+ * and a 16-lane butterfly, the chunk maximum, weights exp(s - max), and the
+ * chunk's weight sum and weighted value sum in a fixed lane and wave order;
+ * across chunks a left-to-right fold in chunk order; then one division.
+ * Row (b, hq) of out depends only on q[b][hq], sequence b's cache and
+ * lens[b]: not on B, on the other sequences, on max_len or on the layout.
+ *   q    bf16 [B][Hq][D], contiguous;
+ *   k, v bf16, element (b, h, t, d) at b*kv_stride_b + h*kv_stride_h +
+ *        t*kv_stride_t + d (D contiguous; "bhtd" and "bthd" caches are both
+ *        expressible), 16-byte aligned, strides multiples of 8;
+ *   lens int32 [B] in device memory;  out fp32 [B][Hq][D], contiguous.
+ * D in {64, 128}; Hq % Hkv == 0 and G <= 16 (EUNSUPPORTED / EINVAL
+ * otherwise).  ws: inv_decode_attention_workspace_bytes(B, Hq, D, max_len)
+ * bytes, 256-byte aligned (EWORKSPACE).  Two launches on s.
+ */
+int inv_decode_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         long kv_stride_b, long kv_stride_h, long kv_stride_t,
+                         const int *lens, float *out, int B, int Hq, int Hkv, int D,
+                         int max_len, float scale, void *ws, size_t ws_bytes,
+                         detred_stream s);
+
 #ifdef __cplusplus
 }
 #endif

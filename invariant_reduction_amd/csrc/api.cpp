@@ -539,4 +539,61 @@ int inv_mean(const float* x, float* y, int rows, int cols, detred_stream s)
     return hip_status(launch_mean(x, y, rows, cols, (hipStream_t)s));
 }
 
+size_t inv_decode_attention_workspace_bytes(int B, int Hq, int D, int max_len)
+{
+    if (B < 0 || Hq <= 0 || D <= 0 || max_len < 0)
+        return 0;
+    const size_t nch = ((size_t)max_len + attention_chunk() - 1) / attention_chunk();
+    const size_t rows = (size_t)B * Hq * nch;
+    return round_up(rows * D * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
+}
+
+int inv_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long kv_stride_b,
+                         long kv_stride_h, long kv_stride_t, const int* lens, float* out, int B,
+                         int Hq, int Hkv, int D, int max_len, float scale, void* ws,
+                         size_t ws_bytes, detred_stream s)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || Hq % Hkv != 0)
+        return DETRED_EINVAL;
+    if (D != 64 && D != 128)
+        return DETRED_EUNSUPPORTED;
+    if (Hq / Hkv > 16)
+        return DETRED_EUNSUPPORTED;
+    if (B == 0)
+        return DETRED_OK;
+    if (!q || !k || !v || !lens || !out || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        ((uintptr_t)lens & 3u) != 0 || ((uintptr_t)q & 1u) != 0)
+        return DETRED_EINVAL;
+    if (kv_stride_b < 0 || kv_stride_h < 0 || kv_stride_t < 0 || kv_stride_b % 8 != 0 ||
+        kv_stride_h % 8 != 0 || kv_stride_t % 8 != 0)
+        return DETRED_EINVAL;
+    const int chunk = attention_chunk();
+    const size_t nch = ((size_t)max_len + chunk - 1) / chunk;
+    if ((size_t)B * Hkv * nch >= ((size_t)1 << 31) || (size_t)B * Hq >= ((size_t)1 << 31))
+        return DETRED_EUNSUPPORTED;
+    const size_t need = inv_decode_attention_workspace_bytes(B, Hq, D, max_len);
+    if (!ws || !aligned256(ws) || ws_bytes < need)
+        return DETRED_EWORKSPACE;
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.sb = kv_stride_b;
+    a.sh = kv_stride_h;
+    a.st = kv_stride_t;
+    a.lens = lens;
+    a.out = out;
+    a.part_o = (float*)ws;
+    a.part_ml = (float*)((char*)ws + round_up((size_t)B * Hq * nch * D * sizeof(float), 256));
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.D = D;
+    a.max_len = max_len;
+    a.nch = (int)nch;
+    a.scale = scale;
+    return hip_status(launch_decode_attention(a, (hipStream_t)s));
+}
+
 }  // extern "C"

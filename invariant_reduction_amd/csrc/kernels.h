@@ -53,6 +53,25 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_
                                int hidden, float eps, hipStream_t s);
 // y = epilogue(p = 0) over an M x N output: the addmm of an empty product
 hipError_t launch_epilogue_only(const GemmArgs& g, hipStream_t s);
+// Decode attention (attention.hip).  q [B][Hq][D] bf16; k, v bf16 with D
+// contiguous, element strides sb, sh, st for sequence, KV head, position;
+// lens [B] int32 on the device; out [B][Hq][D] fp32.  part_o / part_ml:
+// the per-chunk results, [B*Hq][nch][D] and [B*Hq][nch][2] fp32.
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    long sb, sh, st;
+    const int* lens;
+    float* out;
+    float* part_o;
+    float* part_ml;
+    int B, Hq, Hkv, G, D, max_len, nch;
+    float scale;
+};
+int attention_chunk();
+hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s);
+
 hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s);
 hipError_t launch_mean(const float* x, float* y, int rows, int cols, hipStream_t s);
 

@@ -50,6 +50,9 @@ SIGNATURES = {
     "inv_rmsnorm_bf16": ([_P, _P, _P, _I, _I, _F, _P], _I),
     "inv_log_softmax": ([_P, _P, _I, _I, _P], _I),
     "inv_mean": ([_P, _P, _I, _I, _P], _I),
+    "inv_decode_attention_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "inv_decode_attention": ([_P, _P, _P, ctypes.c_long, ctypes.c_long, ctypes.c_long, _P, _P,
+                              _I, _I, _I, _I, _I, _F, _P, _Z, _P], _I),
 }
 
 
@@ -389,3 +392,49 @@ def inv_mean(x, y, stream=None):
     if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.numel() != rows:
         raise TypeError("y must be a contiguous fp32 GPU vector with one element per row")
     return "inv_mean", (px, ctypes.c_void_p(y.data_ptr()), rows, cols, _stream(stream))
+
+
+def inv_decode_attention_workspace_bytes(B, Hq, D, max_len):
+    return int(lib().inv_decode_attention_workspace_bytes(B, Hq, D, max_len))
+
+
+def attention_workspace(B, Hq, D, max_len, device="cuda"):
+    """Allocate (through torch) the inv_decode_attention workspace."""
+    nbytes = inv_decode_attention_workspace_bytes(B, Hq, D, max_len)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+@_entry
+def inv_decode_attention(q, k, v, lens, out, scale, ws, layout="bhtd", stream=None):
+    """out[B,Hq,D] fp32 = decode attention of q[B,Hq,D] (bf16) over the
+    cache k, v (bf16, [B,Hkv,L,D] for layout "bhtd" or [B,L,Hkv,D] for
+    "bthd", any strides with D contiguous) for the first lens[b] (int32 GPU
+    vector) positions, split into fixed chunks of 256 positions."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype not in _BF16_TYPES or not t.is_cuda:
+            raise TypeError("%s must be a bf16 GPU tensor" % n)
+    if lens.dtype != torch.int32 or not lens.is_cuda or not lens.is_contiguous():
+        raise TypeError("lens must be a contiguous int32 GPU vector")
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise TypeError("out must be a contiguous fp32 GPU tensor")
+    if not q.is_contiguous() or q.dim() != 3 or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("q must be contiguous [B,Hq,D]; k and v must share shape and strides")
+    B, Hq, D = q.shape
+    if layout == "bhtd":
+        _, Hkv, L, D2 = k.shape
+        sb, sh, st = k.stride(0), k.stride(1), k.stride(2)
+    elif layout == "bthd":
+        _, L, Hkv, D2 = k.shape
+        sb, sh, st = k.stride(0), k.stride(2), k.stride(1)
+    else:
+        raise ValueError("layout must be 'bhtd' or 'bthd'")
+    if k.stride(3) != 1 or D2 != D or k.shape[0] != B or tuple(out.shape) != (B, Hq, D) or lens.numel() != B:
+        raise ValueError("shape mismatch")
+    pws, nws = _ws(ws)
+    return "inv_decode_attention", (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                      ctypes.c_void_p(v.data_ptr()), sb, sh, st,
+                                      ctypes.c_void_p(lens.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                      B, Hq, Hkv, D, L, float(scale), pws, nws, _stream(stream))

@@ -24,6 +24,9 @@ STREAM_GAMMA = 3
 STREAM_LOGITS = 4
 STREAM_BASE = 5
 STREAM_BIAS = 6
+STREAM_Q = 7
+STREAM_K = 8
+STREAM_V = 9
 
 
 def rng(seed, stream):
@@ -106,3 +109,11 @@ def lora_layer_inputs(M, K, N, r, seed=0):
 def bias_inputs(N, seed=0):
     """An fp32 bias row of N values ~ N(0,1)."""
     return normal_f32((N,), 0.0, 1.0, seed, STREAM_BIAS)
+
+
+def attention_inputs(B, Hq, Hkv, L, D, seed=0):
+    """Decode attention: q[B,Hq,D], k and v [B,Hkv,L,D] ~ N(0,1), bf16 bits."""
+    q = normal_bf16((B, Hq, D), 0.0, 1.0, seed, STREAM_Q)
+    k = normal_bf16((B, Hkv, L, D), 0.0, 1.0, seed, STREAM_K)
+    v = normal_bf16((B, Hkv, L, D), 0.0, 1.0, seed, STREAM_V)
+    return q, k, v

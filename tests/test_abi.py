@@ -186,3 +186,37 @@ def test_addmm_lora_and_bf16_rmsnorm_reject():
     assert L.inv_rmsnorm_bf16(A16, A16b, A16c, 4, 4100, f(1e-6), None) == detred.EUNSUPPORTED
     assert L.inv_rmsnorm_bf16(A16, None, A16c, 4, 4096, f(1e-6), None) == detred.EINVAL
     assert L.inv_rmsnorm_bf16(A16, A16b, MIS, 4, 4096, f(1e-6), None) == detred.EINVAL
+
+
+def test_decode_attention_rejects():
+    L = detred.lib()
+    f = ctypes.c_float
+    WS = 0x100000
+    big = 1 << 40
+    # (q, k, v, sb, sh, st, lens, out, B, Hq, Hkv, D, max_len, scale, ws, nws, s)
+    base = dict(q=A16, k=A16b, v=A16c, sb=8 * 1024 * 128, sh=1024 * 128, st=128, lens=A16,
+                out=A16b, B=2, Hq=8, Hkv=2, D=128, L=1024, ws=WS, nws=big)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.inv_decode_attention(a["q"], a["k"], a["v"], a["sb"], a["sh"], a["st"], a["lens"],
+                                      a["out"], a["B"], a["Hq"], a["Hkv"], a["D"], a["L"], f(0.1),
+                                      a["ws"], a["nws"], None)
+    assert call(Hq=6, Hkv=4) == detred.EINVAL          # Hq % Hkv
+    assert call(Hkv=0) == detred.EINVAL
+    assert call(B=-1) == detred.EINVAL
+    assert call(L=-1) == detred.EINVAL
+    assert call(D=96) == detred.EUNSUPPORTED
+    assert call(Hq=34, Hkv=2) == detred.EUNSUPPORTED    # group of 17
+    assert call(k=MIS) == detred.EINVAL
+    assert call(lens=None) == detred.EINVAL
+    assert call(st=100) == detred.EINVAL                 # row stride not 16-byte aligned
+    assert call(sh=-8) == detred.EINVAL
+    assert call(ws=None) == detred.EWORKSPACE
+    assert call(ws=WS + 16) == detred.EWORKSPACE
+    assert call(nws=16) == detred.EWORKSPACE
+    assert call(B=0, q=None, k=None, v=None, lens=None, out=None) == detred.OK
+    # per-chunk results: B*Hq rows x 4 chunks x (D floats + 2 floats)
+    assert L.inv_decode_attention_workspace_bytes(2, 8, 128, 1024) == 16 * 4 * 128 * 4 + 512
+    assert L.inv_decode_attention_workspace_bytes(2, 8, 128, 1025) == 16 * 5 * 128 * 4 + 768
+    assert L.inv_decode_attention_workspace_bytes(2, 0, 128, 1024) == 0
