@@ -220,3 +220,15 @@ def test_decode_attention_rejects():
     assert L.inv_decode_attention_workspace_bytes(2, 8, 128, 1024) == 16 * 4 * 128 * 4 + 512
     assert L.inv_decode_attention_workspace_bytes(2, 8, 128, 1025) == 16 * 5 * 128 * 4 + 768
     assert L.inv_decode_attention_workspace_bytes(2, 0, 128, 1024) == 0
+
+
+def test_torch_mode_registers_and_restores():
+    # registration only (CPU): entering and leaving the mode; CPU operators
+    # are not affected by the GPU-key replacements
+    import torch
+    from invariant_reduction_amd import torch_ops
+    a = torch.ones(4, 8, dtype=torch.bfloat16)
+    with torch_ops.batch_invariant_mode():
+        assert torch_ops.is_enabled()
+        assert torch.equal(torch.mm(a, a.t()), torch.full((4, 4), 8.0, dtype=torch.bfloat16))
+    assert not torch_ops.is_enabled()
