@@ -162,6 +162,9 @@ __global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x
     const int nv = cols / 4;
     const int lane = tid & 63, wave = tid >> 6;
 
+    // exp of an element: the hardware base-2 exponential of (x - m)*log2(e)
+    // (__expf), relative error about 2e-6 for |x - m| <= 30, a fixed
+    // function like any other; the rescales of the running sum use expf
     float m = -INFINITY, s = 0.0f;
     auto visit = [&](const float4 q) {
         const float mx = fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w));
@@ -169,10 +172,10 @@ __global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x
             s = s * expf(m - mx);
             m = mx;
         }
-        s = s + expf(q.x - m);
-        s = s + expf(q.y - m);
-        s = s + expf(q.z - m);
-        s = s + expf(q.w - m);
+        s = s + __expf(q.x - m);
+        s = s + __expf(q.y - m);
+        s = s + __expf(q.z - m);
+        s = s + __expf(q.w - m);
     };
 
     // vectors 0 .. LSM_REG-1 of the thread: all loads issued, then visited
