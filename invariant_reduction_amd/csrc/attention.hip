@@ -9,9 +9,9 @@
 //
 //   chunk pass, one workgroup per (sequence b, KV head h, chunk j), for the
 //   G = Hq/Hkv query heads of h:
-//     s_t   = (sum over d of q_d * k_td) * scale: per position, 16 lanes
+//     s_t   = (sum over d of q_d * k_td) * scale: per position, D/8 lanes
 //             each take 8 consecutive d in a fused multiply-add chain, then
-//             a butterfly over the 16 lanes;
+//             a fixed tree of DPP adds over those lanes, read from the first;
 //     m_j   = max of s_t over the chunk (exact);
 //     p_t   = exp(s_t - m_j);   l_j = sum of p_t (per lane 4 positions in
 //             order, then a wave butterfly);
@@ -40,6 +40,35 @@ constexpr int THREADS = 256;
 static_assert(CHUNK == 4 * 64, "the softmax pass gives each lane four positions");
 
 __device__ __forceinline__ float bf16_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Cross-lane moves within a row of 16 lanes (DPP): a rotation of the row,
+// a mirror of each half row, and two quad permutations.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_ROW_ROR8 = 0x128, DPP_ROW_ROR4 = 0x124, DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_QUAD_XOR2 = 0x4e, DPP_QUAD_XOR1 = 0xb1;
+
+// Sum over the DG consecutive lanes holding one position's pieces (DG = 16:
+// a row; DG = 8: a half row), a fixed tree; the first lane of the group
+// holds the result.  16 lanes: ror 8, ror 4, then lanes xor 2, xor 1;
+// 8 lanes: mirror, then xor 2, xor 1.
+template <int DG>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(DG == 8 || DG == 16, "8 or 16 lanes per position");
+    if constexpr (DG == 16) {
+        v = v + dpp<DPP_ROW_ROR8>(v);
+        v = v + dpp<DPP_ROW_ROR4>(v);
+    } else {
+        v = v + dpp<DPP_ROW_HALF_MIRROR>(v);
+    }
+    v = v + dpp<DPP_QUAD_XOR2>(v);
+    v = v + dpp<DPP_QUAD_XOR1>(v);
+    return v;
+}
 
 __device__ __forceinline__ void unpack8(const uint4 q, float (&f)[8])
 {
@@ -88,37 +117,48 @@ __global__ __launch_bounds__(THREADS) void chunk_kernel(AttnArgs a)
     const uint16_t* vb = a.v + base;
     const int dg = tid % DG, tl = tid / DG;
 
-    // scores: all of a thread's key pieces are loaded before the products
-    uint4 kq[ITER];
+    // this thread's 8 query dimensions of every head, in registers when
+    // they fit
+    constexpr bool QREG = GM <= 8;
+    float qr[QREG ? GM : 1][8];
+    if constexpr (QREG) {
 #pragma unroll
-    for (int r = 0; r < ITER; ++r) {
-        const int t = r * TPI + tl;
-        kq[r] = t < nv ? *reinterpret_cast<const uint4*>(kb + (size_t)t * a.st + dg * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int r = 0; r < ITER; ++r) {
-        const int t = r * TPI + tl;
-        float kf[8];
-        unpack8(kq[r], kf);
-        float part[GM];
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            float s = 0.0f;
+        for (int g = 0; g < GM; ++g)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s = fmaf(qs[g][dg * 8 + e], kf[e], s);
-            part[g] = s;
+                qr[g][e] = qs[g][dg * 8 + e];
+    }
+    // scores, in two batches: all key pieces of a batch are loaded before
+    // its products
+    constexpr int IB = ITER / 2;
+#pragma unroll
+    for (int h0 = 0; h0 < ITER; h0 += IB) {
+        uint4 kq[IB];
+#pragma unroll
+        for (int r = 0; r < IB; ++r) {
+            const int t = (h0 + r) * TPI + tl;
+            kq[r] = t < nv ? *reinterpret_cast<const uint4*>(kb + (size_t)t * a.st + dg * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int off = DG / 2; off > 0; off >>= 1)
+        for (int r = 0; r < IB; ++r) {
+            const int t = (h0 + r) * TPI + tl;
+            float kf[8];
+            unpack8(kq[r], kf);
+            float part[GM];
 #pragma unroll
-            for (int g = 0; g < GM; ++g)
-                part[g] = part[g] + __shfl_xor(part[g], off, 64);
-        if (dg == 0) {
+            for (int g = 0; g < GM; ++g) {
+                float s = 0.0f;
 #pragma unroll
-            for (int g = 0; g < GM; ++g)
-                sc[g][t] = t < nv ? part[g] * a.scale : -INFINITY;
+                for (int e = 0; e < 8; ++e)
+                    s = fmaf(QREG ? qr[QREG ? g : 0][e] : qs[g][dg * 8 + e], kf[e], s);
+                part[g] = group_sum<DG>(s);
+            }
+            if (dg == 0) {
+#pragma unroll
+                for (int g = 0; g < GM; ++g)
+                    sc[g][t] = t < nv ? part[g] * a.scale : -INFINITY;
+            }
         }
     }
     __syncthreads();
@@ -224,13 +264,27 @@ __global__ __launch_bounds__(D) void fold_kernel(AttnArgs a)
     const float* ml = a.part_ml + bh * a.nch * 2;
     const float* po = a.part_o + bh * a.nch * D + d;
     float M = ml[0], L = ml[1], O = po[0];
-    for (int jj = 1; jj < n; ++jj) {
-        const float mj = ml[2 * jj], lj = ml[2 * jj + 1], oj = po[(size_t)jj * D];
-        const float Mn = fmaxf(M, mj);
-        const float ca = expf(M - Mn), cb = expf(mj - Mn);
-        L = L * ca + lj * cb;
-        O = O * ca + oj * cb;
-        M = Mn;
+    // FB chunks' results are loaded before they are folded, in chunk order
+    constexpr int FB = 8;
+    for (int j0 = 1; j0 < n; j0 += FB) {
+        float mj[FB], lj[FB], oj[FB];
+#pragma unroll
+        for (int u = 0; u < FB; ++u) {
+            const int jj = j0 + u < n ? j0 + u : n - 1;
+            mj[u] = ml[2 * jj];
+            lj[u] = ml[2 * jj + 1];
+            oj[u] = po[(size_t)jj * D];
+        }
+#pragma unroll
+        for (int u = 0; u < FB; ++u) {
+            if (j0 + u < n) {
+                const float Mn = fmaxf(M, mj[u]);
+                const float ca = expf(M - Mn), cb = expf(mj[u] - Mn);
+                L = L * ca + lj[u] * cb;
+                O = O * ca + oj[u] * cb;
+                M = Mn;
+            }
+        }
     }
     a.out[bh * D + d] = O / L;
 }
