@@ -1,6 +1,7 @@
 // LDS-DMA slice GEMM engine for gfx950: the 128x128 workgroup tile used for
-// wide outputs.  Same reduction order and epilogues as the register-staged
-// engine (gemm_common.h); only the data movement differs:
+// wide outputs.  Same reduction order, output values and last-arriver
+// combine as the register-staged engine (gemm_common.h); the data movement
+// differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
 //    STAGES K blocks of 64 in flight; the buffer descriptors' record counts
@@ -17,7 +18,10 @@
 //  * both layouts XOR-swizzle 16-byte chunks within a row so that the
 //    fragment reads spread over the LDS banks (the DMA writes each wave's
 //    1 KiB contiguously, so the swizzle is chosen by which global chunk
-//    each lane fetches).
+//    each lane fetches);
+//  * the finished tile goes out through the stage buffers as whole 16-byte
+//    row pieces (store_tile_via_lds), with the addmm epilogue applied on the
+//    way when the call asks for it.
 //
 // Requires every 32-wide MFMA step to lie inside K (K % 32 == 0 when K is
 // one chunk; always true with 8 chunks), so no step needs zero padding.
