@@ -91,7 +91,9 @@ int detred_version(void);
  * The locked policy for a product with N output columns and reduction
  * length K (it never depends on M).  Writes, where the pointer is non-NULL:
  *   chunks   = P (1 or 8) and chunk_k = Kc;
- *   tile_m, tile_n = the workgroup output tile;
+ *   tile_m, tile_n = the workgroup output tile for large M (an output of at
+ *                    most 64 columns with few rows may run on 64 x 16 tiles;
+ *                    no tile changes the bits);
  *   default_split  = the split split_k = 0 picks once M is large enough to
  *                    give every CU an output tile (detred_auto_split).
  * Returns EINVAL for N < 0 or K < 0.
