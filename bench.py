@@ -15,10 +15,15 @@ vocabulary 151936), batch 256:
                                      (what the cross-rank reduction computes)
   log_softmax  inv_log_softmax       logits[256,151936] fp32
   mean         inv_mean              logits[256,151936] fp32
-Every operation runs in libdetred's HIP kernels.  `value` is the
-deterministic GEMM work of a step (shrink, expand, dense, tree-TP) divided
-by the step time.  Each operation is also timed alone with HIP events on the
-stream it runs on; the slowest one gets the roofline object.
+Every operation runs in libdetred's HIP kernels.  The step's three
+independent chains (dense -> log_softmax; the tree-TP pair; rmsnorm, the
+LoRA shrink/control/cast/expand and mean) run on three streams of default
+priority, forked from and joined to the main stream with events; the same
+ops issued serially on one stream are timed too (ms_per_step_serial).
+`value` is the deterministic GEMM work of a step (shrink, expand, dense,
+tree-TP) divided by the step time.  Each operation is also timed alone
+with HIP events on the stream it runs on; the slowest one gets the roofline
+object.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -90,45 +95,74 @@ class Workload:
         self.p_tp = torch.empty((TP_T, TP_M, TP_N), dtype=f32, device=dev)
         self.ws_dns = detred.workspace(B, F, H, 0, dev)
 
-    def ops(self):
-        """(name, launch, det-GEMM flops, algorithmic bytes) in step order.
-        Each launch re-issues a C call whose arguments were marshalled once."""
+    def ops(self, streams):
+        """(name, launch, det-GEMM flops, algorithmic bytes, lane) in step
+        order.  Each launch re-issues a C call whose arguments were
+        marshalled once, on streams[lane].  Lanes are independent chains:
+        0 dense -> log_softmax; 1 the tree-TP pair; 2 rmsnorm, the LoRA
+        shrink/control/cast/expand and mean."""
         gb = 2  # bytes per bf16
-        P = detred.prepare
+
+        def P(lane, fn, *args):
+            return detred.prepare(fn, *args, stream=streams[lane])
         return [
-            ("rmsnorm", P(detred.inv_rmsnorm, self.x, self.g, self.y_rms, 1e-6),
-             0, B * H * gb + H * gb + B * H * 4),
-            ("shrink", P(detred.det_splitk_gemm, self.X, self.A, self.y_shr, 8, self.ws_shr),
-             2 * B * H * R, B * H * gb + H * R * gb + B * R * 4),
-            ("shrink_atom", P(detred.atomic_splitk_gemm, self.X, self.A, self.y_atm, 8),
-             0, B * H * gb + H * R * gb + B * R * 4),
-            ("cast", P(detred.detred_f32_to_bf16, self.y_shr, self.y_b16),
-             0, B * R * 4 + B * R * gb),
-            ("expand", P(detred.det_splitk_gemm, self.y_b16, self.B, self.y_exp, 0),
-             2 * B * R * H, B * R * gb + R * H * gb + B * H * 4),
-            ("dense", P(detred.det_splitk_gemm, self.X, self.W, self.y_dns, 0, self.ws_dns),
-             2 * B * H * F, B * H * gb + H * F * gb + B * F * 4),
-            ("tp_shards", P(detred.tree_tp_shards_gemm, self.Xt, self.Wt, self.p_tp, TP_T),
-             2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_T * TP_M * TP_N * 4),
-            ("tp_combine", P(detred.tree_combine_f32, self.p_tp, self.y_tp),
-             0, TP_T * TP_M * TP_N * 4 + TP_M * TP_N * 4),
-            ("log_softmax", P(detred.inv_log_softmax, self.lg, self.y_lsm),
-             0, 2 * B * V * 4),
-            ("mean", P(detred.inv_mean, self.lg, self.y_mean),
-             0, B * V * 4 + B * 4),
+            ("rmsnorm", P(2, detred.inv_rmsnorm, self.x, self.g, self.y_rms, 1e-6),
+             0, B * H * gb + H * gb + B * H * 4, 2),
+            ("shrink", P(2, detred.det_splitk_gemm, self.X, self.A, self.y_shr, 8, self.ws_shr),
+             2 * B * H * R, B * H * gb + H * R * gb + B * R * 4, 2),
+            ("shrink_atom", P(2, detred.atomic_splitk_gemm, self.X, self.A, self.y_atm, 8),
+             0, B * H * gb + H * R * gb + B * R * 4, 2),
+            ("cast", P(2, detred.detred_f32_to_bf16, self.y_shr, self.y_b16),
+             0, B * R * 4 + B * R * gb, 2),
+            ("expand", P(2, detred.det_splitk_gemm, self.y_b16, self.B, self.y_exp, 0),
+             2 * B * R * H, B * R * gb + R * H * gb + B * H * 4, 2),
+            ("dense", P(0, detred.det_splitk_gemm, self.X, self.W, self.y_dns, 0, self.ws_dns),
+             2 * B * H * F, B * H * gb + H * F * gb + B * F * 4, 0),
+            ("tp_shards", P(1, detred.tree_tp_shards_gemm, self.Xt, self.Wt, self.p_tp, TP_T),
+             2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_T * TP_M * TP_N * 4, 1),
+            ("tp_combine", P(1, detred.tree_combine_f32, self.p_tp, self.y_tp),
+             0, TP_T * TP_M * TP_N * 4 + TP_M * TP_N * 4, 1),
+            ("log_softmax", P(0, detred.inv_log_softmax, self.lg, self.y_lsm),
+             0, 2 * B * V * 4, 0),
+            ("mean", P(2, detred.inv_mean, self.lg, self.y_mean),
+             0, B * V * 4 + B * 4, 2),
         ]
 
 
-def time_steps(ops, steps, stream):
+class Step:
+    """One step: the ops issued in order, each on its lane's stream; the
+    side streams wait for the main stream before their first op and the
+    main stream waits for them after their last (events, no host sync)."""
+
+    def __init__(self, ops, streams):
+        self.ops = ops
+        self.streams = streams
+        self.fork = torch.cuda.Event()
+        self.join = [torch.cuda.Event() for _ in streams]
+
+    def __call__(self):
+        main = self.streams[0]
+        if len(self.streams) > 1:
+            self.fork.record(main)
+            for s in self.streams[1:]:
+                s.wait_event(self.fork)
+        for op in self.ops:
+            op[1]()
+        if len(self.streams) > 1:
+            for s, e in zip(self.streams[1:], self.join[1:]):
+                e.record(s)
+                main.wait_event(e)
+
+
+def time_steps(step, steps, stream):
     """Whole-region time of `steps` passes, bracketed by one HIP event pair
-    on the stream the kernels run on."""
+    on the main stream (which joins every side stream each step)."""
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(steps):
-        for _, fn, _, _ in ops:
-            fn()
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1)
@@ -136,14 +170,14 @@ def time_steps(ops, steps, stream):
 
 def time_ops(ops, steps, stream):
     """Per-launch durations: a HIP event pair around every launch of a
-    second pass of `steps` steps."""
+    pass of `steps` serial steps (every op on `stream`, one at a time)."""
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in ops] for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
-        for i, (_, fn, _, _) in enumerate(ops):
+        for i, op in enumerate(ops):
             ev[s][i][0].record(stream)
-            fn()
+            op[1]()
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
     return [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)] for i in range(len(ops))]
@@ -442,21 +476,29 @@ def main():
 
     print("bench: generating inputs", file=sys.stderr, flush=True)
     wl = Workload(dev)
-    ops = wl.ops()
+    # the step's three independent chains on three streams (default
+    # priority), and the same ops all on the main stream for the serial
+    # step and the per-op timings
+    lanes = [stream, torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    ops = wl.ops(lanes)
+    serial_ops = wl.ops([stream, stream, stream])
+    step = Step(ops, lanes)
+    serial = Step(serial_ops, [stream])
     for _ in range(args.warmup):
-        for _, fn, _, _ in ops:
-            fn()
+        step()
+        serial()
     torch.cuda.synchronize()
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
 
-    total_ms = time_steps(ops, args.steps, stream)
+    total_ms = time_steps(step, args.steps, stream)
     ms_per_step = total_ms / args.steps
-    per_op = time_ops(ops, args.steps, stream)
-    det_flops = sum(f for _, _, f, _ in ops)
+    ms_serial = time_steps(serial, args.steps, stream) / args.steps
+    per_op = time_ops(serial_ops, args.steps, stream)
+    det_flops = sum(op[2] for op in ops)
     value = det_flops / (ms_per_step * 1e-3) / 1e12
 
     op_stats = {}
-    for (name, _, fl, by), ts in zip(ops, per_op):
+    for (name, _, fl, by, _), ts in zip(ops, per_op):
         avg = sum(ts) / len(ts)
         srt = sorted(ts)
         st = {"avg_us": round(avg * 1000, 2), "median_us": round(statistics.median(ts) * 1000, 2),
@@ -467,7 +509,7 @@ def main():
         st["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         op_stats[name] = st
     dom_i = max(range(len(ops)), key=lambda i: sum(per_op[i]))
-    dname, _, dfl, dby = ops[dom_i]
+    dname, _, dfl, dby, _ = ops[dom_i]
     davg_s = sum(per_op[dom_i]) / len(per_op[dom_i]) * 1e-3
     if dfl and dfl / dby >= RIDGE:
         roof = {"bound": "mfma", "achieved": round(dfl / davg_s / 1e12, 2),
@@ -496,8 +538,7 @@ def main():
     atom0 = None
     det_same = atom_diff = 0
     for r in range(20):
-        for _, fn, _, _ in ops:
-            fn()
+        step()
         torch.cuda.synchronize()
         det_same += all(torch.equal(getattr(wl, k).view(torch.int32), v.view(torch.int32))
                         for k, v in ref.items())
@@ -520,6 +561,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_serial": round(ms_serial, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
