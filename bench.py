@@ -453,6 +453,9 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the timed steps (for profiler runs): no ratios, "
                          "invariance checks, breakdown or CPU baseline")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue every op on the main stream (no overlap between kernels, "
+                         "so a profiler's per-kernel durations match the per-op timings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (HBM counter calibration)")
     args = ap.parse_args()
@@ -480,7 +483,9 @@ def main():
     # priority), and the same ops all on the main stream for the serial
     # step and the per-op timings
     lanes = [stream, torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
-    ops = wl.ops(lanes)
+    if args.serial:
+        lanes = [stream]
+    ops = wl.ops(lanes * 3 if args.serial else lanes)
     serial_ops = wl.ops([stream, stream, stream])
     step = Step(ops, lanes)
     serial = Step(serial_ops, [stream])
