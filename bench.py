@@ -97,7 +97,9 @@ class Workload:
 
     def ops(self, streams):
         """(name, launch, det-GEMM flops, algorithmic bytes, lane) in step
-        order.  Each launch re-issues a C call whose arguments were
+        order.  Algorithmic bytes count inputs and the final output once;
+        split partials and shard buffers are not credited (tp_shards: X, W
+        and one [M,N] result).  Each launch re-issues a C call whose arguments were
         marshalled once, on streams[lane].  Lanes are independent chains:
         0 dense -> log_softmax; 1 the tree-TP pair; 2 rmsnorm, the LoRA
         shrink/control/cast/expand and mean."""
@@ -119,7 +121,7 @@ class Workload:
             ("dense", P(0, detred.det_splitk_gemm, self.X, self.W, self.y_dns, 0, self.ws_dns),
              2 * B * H * F, B * H * gb + H * F * gb + B * F * 4, 0),
             ("tp_shards", P(1, detred.tree_tp_shards_gemm, self.Xt, self.Wt, self.p_tp, TP_T),
-             2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_T * TP_M * TP_N * 4, 1),
+             2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_M * TP_N * 4, 1),
             ("tp_combine", P(1, detred.tree_combine_f32, self.p_tp, self.y_tp),
              0, TP_T * TP_M * TP_N * 4 + TP_M * TP_N * 4, 1),
             ("log_softmax", P(0, detred.inv_log_softmax, self.lg, self.y_lsm),
@@ -391,6 +393,76 @@ def extensions(dev, stream):
     return out
 
 
+def config_sweep(dev, stream):
+    """The measurement table of the configurations: each call timed alone
+    (median of 20 after 3 warm-ups, HIP events), with its roofline time
+    max(flop / 2.5 PF/s, algorithmic bytes / 8 TB/s) and the fraction
+    roofline / measured.  Inputs are drawn on the device from seeded
+    generators with the configurations' distributions."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    gb = 2
+    out = {}
+
+    def bf(shape, std):
+        return (torch.randn(shape, device=dev, generator=gen) * std).to(torch.bfloat16)
+
+    def rec(name, fn, flops, nbytes):
+        med = median_time_us(fn, 20, stream, warm=3)[0]
+        roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+        out[name] = {"us": round(med, 2), "roofline_us": round(roof, 2),
+                     "bound": "mfma" if flops / max(nbytes, 1) >= RIDGE else "hbm",
+                     "frac": round(roof / med, 4)}
+
+    # LoRA shrink (det split-K = 8) and expand, M x r
+    for r in (16, 64):
+        A = bf((H, r), 0.02)
+        Bm = bf((r, H), 0.02)
+        for M in (1, 8, 64, 256):
+            X = bf((M, H), 1.0)
+            Y = torch.empty((M, r), dtype=torch.float32, device=dev)
+            rec("shrink_m%d_r%d" % (M, r),
+                detred.prepare(detred.det_splitk_gemm, X, A, Y, 8, detred.workspace(M, r, H, 8, dev)),
+                2 * M * H * r, M * H * gb + H * r * gb + M * r * 4)
+            Z = torch.empty((M, H), dtype=torch.float32, device=dev)
+            Yb = bf((M, r), 1.0)
+            rec("expand_m%d_r%d" % (M, r), detred.prepare(detred.det_splitk_gemm, Yb, Bm, Z, 0),
+                2 * M * r * H, M * r * gb + r * H * gb + M * H * 4)
+    # dense X[M,4096] W[4096,14336], automatic split
+    W = bf((H, F), 0.02)
+    for M in (1, 16, 128, 1024, 4096):
+        X = bf((M, H), 1.0)
+        Y = torch.empty((M, F), dtype=torch.float32, device=dev)
+        rec("dense_m%d" % M, detred.prepare(detred.det_splitk_gemm, X, W, Y, 0,
+                                            detred.workspace(M, F, H, 0, dev)),
+            2 * M * H * F, M * H * gb + H * F * gb + M * F * 4)
+    del W
+    # tree-TP X[512,8192] W[8192,8192], both phases
+    Xt, Wt = bf((TP_M, TP_K), 1.0), bf((TP_K, TP_N), 0.02)
+    Yt = torch.empty((TP_M, TP_N), dtype=torch.float32, device=dev)
+    for T in (1, 2, 4, 8):
+        rec("tree_tp_T%d" % T, detred.prepare(detred.tree_tp_gemm, Xt, Wt, Yt, T,
+                                             detred.workspace(TP_M, TP_N, TP_K, T, dev)),
+            2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_M * TP_N * 4)
+    del Xt, Wt
+    # row ops
+    g = (1.0 + 0.1 * torch.randn((H,), device=dev, generator=gen)).to(torch.bfloat16)
+    for Bn in (1, 16, 256, 4096):
+        x = bf((Bn, H), 1.0)
+        y = torch.empty((Bn, H), dtype=torch.float32, device=dev)
+        rec("rmsnorm_b%d" % Bn, detred.prepare(detred.inv_rmsnorm, x, g, y, 1e-6),
+            0, Bn * H * gb + H * gb + Bn * H * 4)
+    for Bn in (256, 4096):
+        lg = torch.randn((Bn, V), device=dev, generator=gen) * 3.0
+        ys = torch.empty_like(lg)
+        rec("log_softmax_b%d" % Bn, detred.prepare(detred.inv_log_softmax, lg, ys), 0, 2 * Bn * V * 4)
+        del ys
+        ym = torch.empty((Bn,), dtype=torch.float32, device=dev)
+        rec("mean_b%d" % Bn, detred.prepare(detred.inv_mean, lg, ym), 0, Bn * V * 4 + Bn * 4)
+        del lg
+    return out
+
+
 def source_hash():
     """Hash of the kernel sources, to tell whether committed counter data
     were taken on the kernels that run now."""
@@ -526,7 +598,7 @@ def main():
     roof["traffic"] = measured_traffic(dname)
     roof["kernel"] = dname
 
-    ratios = tp = div = ext = None
+    ratios = tp = div = ext = sweep = None
     same = total = 0
     if not args.quick:
         print("bench: latency ratios, invariance, tree-TP breakdown", file=sys.stderr, flush=True)
@@ -536,6 +608,8 @@ def main():
         div = divergence(dev, stream)
         print("bench: next-row operations", file=sys.stderr, flush=True)
         ext = extensions(dev, stream)
+        print("bench: configuration sweep", file=sys.stderr, flush=True)
+        sweep = config_sweep(dev, stream)
 
     # replays: every deterministic output is reproduced bit for bit; the
     # atomic control is counted
@@ -579,6 +653,7 @@ def main():
         "det_vs_atomic": ratios,
         "replay_divergence": div,
         "extensions": ext,
+        "configs": sweep,
         "tree_tp_breakdown": tp,
         "bit_invariant_rows_pct": round(100.0 * same / max(total, 1), 4),
         "bit_invariant_rows_checked": total,

@@ -36,7 +36,10 @@ struct Tile {
     static_assert(BK % 32 == 0, "K block must hold whole MFMA steps");
 };
 
-using TileS16 = Tile<64, 16, 4, 1, 64>;
+// The narrow tile stages 256-wide K blocks: a LoRA slice (512 k) is then
+// two global-load round trips instead of eight (shrink at 8 slices, M = 1:
+// 10.8 -> 8.0 us).  The block width never changes the bits.
+using TileS16 = Tile<64, 16, 4, 1, 256>;
 using TileM64 = Tile<64, 64, 2, 2, 64>;
 using TileL128 = Tile<128, 128, 2, 2, 64>;
 
