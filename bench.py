@@ -532,7 +532,7 @@ def main():
                     help="run one 256 MiB device copy first (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
