@@ -200,6 +200,26 @@ def median_time_us(fn, reps, stream, warm=20):
     return ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
 
 
+def cold_time_us(fn, reps, stream, flush):
+    """Median of reps calls, each after a read of `flush` (a 512 MiB
+    buffer, twice the MALL, written once beforehand so that its lines are
+    clean), so the call's operands come from HBM and no write-back of
+    dirty lines overlaps it."""
+    fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            flush.sum()
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+    return ts[len(ts) // 2]
+
+
 def latency_ratios(dev, stream):
     """Deterministic split-K=8 vs atomic split-K=8 (zero fill included) vs
     unsplit, on the LoRA shrink shapes; interleaved, medians of 200."""
@@ -403,16 +423,18 @@ def config_sweep(dev, stream):
     gen.manual_seed(0)
     gb = 2
     out = {}
+    flush = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
 
     def bf(shape, std):
         return (torch.randn(shape, device=dev, generator=gen) * std).to(torch.bfloat16)
 
     def rec(name, fn, flops, nbytes):
         med = median_time_us(fn, 20, stream, warm=3)[0]
+        cold = cold_time_us(fn, 10, stream, flush)
         roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
-        out[name] = {"us": round(med, 2), "roofline_us": round(roof, 2),
+        out[name] = {"us": round(med, 2), "us_cold": round(cold, 2), "roofline_us": round(roof, 2),
                      "bound": "mfma" if flops / max(nbytes, 1) >= RIDGE else "hbm",
-                     "frac": round(roof / med, 4)}
+                     "frac": round(roof / med, 4), "frac_cold": round(roof / cold, 4)}
 
     # LoRA shrink (det split-K = 8) and expand, M x r
     for r in (16, 64):
@@ -488,6 +510,18 @@ def measured_traffic(kernel_op):
     return t.get("ops", {}).get(kernel_op)
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, min_seconds=10.0):
     """The oracle as it stands, on the host cores: one full step of the same
     workload (every row of every operation), repeated until min_seconds."""
@@ -511,7 +545,7 @@ def cpu_baseline(wl, min_seconds=10.0):
             break
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": "%d full step(s) of the same workload in fp64 (all rows of shrink, expand, "
                       "dense, tree-TP, rmsnorm, log_softmax, mean); %.1f s" % (reps, dt)}
 

@@ -74,6 +74,9 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs& g, int bm, int b
 // Device-scope coherence bit (sc1) of the cache-policy operand of buffer
 // loads and stores on gfx950.
 constexpr int CPOL_SC1 = 16;
+// Non-temporal bit (nt): the line is not kept in the caches after the
+// store, so large outputs do not evict the operands still being read.
+constexpr int CPOL_NT = 2;
 // Raw buffer descriptor word 3: 32-bit data format, no swizzle.
 constexpr int RAW_BUFFER_FLAGS = 0x00020000;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

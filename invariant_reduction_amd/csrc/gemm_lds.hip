@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace detred {
@@ -155,7 +157,10 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af
 // four row groups of a 16 x 16 result land in different banks; then every
 // thread stores whole 16-byte row pieces, 32 lanes per 512-byte tile row.
 // COHERENT: device-coherent (sc1) buffer stores, for partials that another
-// workgroup combines.  Needs STAGES * STAGE_BYTES >= 64 KiB.
+// workgroup combines; shard roots (several planes, out_z_stride set) with
+// plain stores, as the cross-shard combine reads them next; final outputs
+// non-temporal (kept in the caches, a large output pushes out the operands
+// still being read).  Needs STAGES * STAGE_BYTES >= 64 KiB.
 template <bool COHERENT>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
                                                    float* out, int ld, int row0, int col0,
@@ -194,14 +199,23 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], c
     if (COHERENT || !g.epi) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             out + (size_t)row0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+        auto put = [&](auto policy) {
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int v = tid + i * THREADS;
-            const int r = v / (BN / 4), c4 = v % (BN / 4);
-            const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
-            const int off = in ? (r * ld + 4 * c4) * 4 : OOB;
-            __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, COHERENT ? CPOL_SC1 : 0);
-        }
+            for (int i = 0; i < ITER; ++i) {
+                const int v = tid + i * THREADS;
+                const int r = v / (BN / 4), c4 = v % (BN / 4);
+                const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
+                const int off = in ? (r * ld + 4 * c4) * 4 : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, decltype(policy)::value);
+            }
+        };
+        if (COHERENT)
+            put(std::integral_constant<int, CPOL_SC1>());
+        else if (g.out_z_stride)
+            // shard roots: the cross-shard combine reads them next
+            put(std::integral_constant<int, 0>());
+        else
+            put(std::integral_constant<int, CPOL_NT>());
         return;
     }
     // the final product of a single-slice addmm: y = beta*C + alpha*p
@@ -237,12 +251,12 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], c
             const u32x2 o = {f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16),
                              f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16)};
             __builtin_amdgcn_raw_buffer_store_b64(o, ry, in ? (int)((r * g.ldy + 4 * c4) * 2) : OOB,
-                                                  0, 0);
+                                                  0, CPOL_NT);
         } else {
             const u32x4 o = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
                              __float_as_uint(y[3])};
             __builtin_amdgcn_raw_buffer_store_b128(o, ry, in ? (int)((r * g.ldy + 4 * c4) * 4) : OOB,
-                                                   0, 0);
+                                                   0, CPOL_NT);
         }
     }
 }
