@@ -172,6 +172,26 @@ int det_splitk_addmm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
                      int split_k, void *ws, size_t ws_bytes, detred_stream s);
 
 /*
+ * det_splitk_gemm and det_splitk_addmm with the weight given transposed:
+ * Wt is [N,K] bf16, K contiguous, rows ldwt elements apart (ldwt >= K,
+ * ldwt % 8 == 0, 16-byte aligned) -- the layout in which a linear layer
+ * keeps its weight ([out, in]), so y = x W^T needs no transposed copy when
+ * the kernels stand in for mm/addmm under an unchanged model ("Batch
+ * Invariant Ops", How It Works).  Element (k, n) of the
+ * product's right operand is Wt[n*ldwt + k].  The products, the chunk tree
+ * and the split rules are those of the untransposed calls, so the output
+ * bits equal theirs for W = Wt^T; workspace, errors and asynchrony as there
+ * (EINVAL also for ldwt < K).
+ */
+int det_splitk_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt,
+                       float *Y, int ldy, int M, int N, int K, int split_k,
+                       void *ws, size_t ws_bytes, detred_stream s);
+int det_splitk_addmm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt,
+                        const float *C, int ldc, float alpha, float beta,
+                        void *Y, int ldy, int y_dtype, int M, int N, int K,
+                        int split_k, void *ws, size_t ws_bytes, detred_stream s);
+
+/*
  * Workspace of det_lora_forward for an M x N layer output with input width K
  * and LoRA rank r: the fp32 base product, the fp32 shrink output, its bf16
  * cast and the split-K workspaces of the base product and the shrink, each

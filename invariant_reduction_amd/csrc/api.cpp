@@ -77,13 +77,14 @@ size_t counter_bytes(const Policy& p, int M, int N)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DETRED_OK : DETRED_EHIP; }
 
-// Checks shared by the GEMM entry points.
+// Checks shared by the GEMM entry points (wt: W given transposed, [N][K]
+// with rows ldw apart).
 int check_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* Y, int ldy,
-               int M, int N, int K)
+               int M, int N, int K, bool wt = false)
 {
     if (M < 0 || N < 0 || K < 0)
         return DETRED_EINVAL;
-    if (ldx < K || ldw < N || ldy < N || ldx < 0 || ldw < 0 || ldy < 0)
+    if (ldx < K || ldw < (wt ? K : N) || ldy < N || ldx < 0 || ldw < 0 || ldy < 0)
         return DETRED_EINVAL;
     if (M == 0 || N == 0)
         return DETRED_OK;
@@ -106,6 +107,7 @@ GemmArgs make_args(const Policy& p, const uint16_t* X, int ldx, const uint16_t* 
     g.ldx = ldx;
     g.W = W;
     g.ldw = ldw;
+    g.wt = 0;
     g.Y = Y;
     g.ldy = ldy;
     g.out_z_stride = 0;
@@ -291,28 +293,34 @@ LoraLayout lora_layout(int M, int N, int K, int r)
 
 extern "C" {
 
-int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
-                    int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+}  // extern "C"
+
+namespace {
+
+int det_gemm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* Y,
+                  int ldy, int M, int N, int K, int split_k, void* ws, size_t ws_bytes,
+                  detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     const Policy p = plan(M, N, K);
     int S = 0;
     if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
         return st;
-    const GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
+    GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
+    g.wt = wt;
     return run_det(p, g, S, ws, ws_bytes, (hipStream_t)s);
 }
 
-int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* C,
-                     int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype, int M, int N,
-                     int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+int det_addmm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt,
+                   const float* C, int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype,
+                   int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
 {
     int st = check_epilogue(C, ldc, N, y_dtype);
     if (st != DETRED_OK)
         return st;
-    st = check_gemm(X, ldx, W, ldw, (const float*)Y, ldy, M, N, K);
+    st = check_gemm(X, ldx, W, ldw, (const float*)Y, ldy, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     const Policy p = plan(M, N, K);
@@ -320,6 +328,7 @@ int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
     if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
         return st;
     GemmArgs g = make_args(p, X, ldx, W, ldw, (float*)Y, ldy, M, N, K, S);
+    g.wt = wt;
     g.epi = 1;
     g.C = C;
     g.ldc = ldc;
@@ -327,6 +336,39 @@ int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
     g.beta = beta;
     g.out_bf16 = (y_dtype == DETRED_BF16);
     return run_det(p, g, S, ws, ws_bytes, (hipStream_t)s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
+                    int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+{
+    return det_gemm_impl(X, ldx, W, ldw, false, Y, ldy, M, N, K, split_k, ws, ws_bytes, s);
+}
+
+int det_splitk_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* Y,
+                       int ldy, int M, int N, int K, int split_k, void* ws, size_t ws_bytes,
+                       detred_stream s)
+{
+    return det_gemm_impl(X, ldx, Wt, ldwt, true, Y, ldy, M, N, K, split_k, ws, ws_bytes, s);
+}
+
+int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* C,
+                     int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype, int M, int N,
+                     int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+{
+    return det_addmm_impl(X, ldx, W, ldw, false, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K,
+                          split_k, ws, ws_bytes, s);
+}
+
+int det_splitk_addmm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, const float* C,
+                        int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype, int M,
+                        int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+{
+    return det_addmm_impl(X, ldx, Wt, ldwt, true, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K,
+                          split_k, ws, ws_bytes, s);
 }
 
 size_t det_lora_workspace_bytes(int M, int N, int K, int r)

@@ -32,6 +32,8 @@ struct Tile {
     static constexpr int A_PER_THREAD = (A_VECS + THREADS - 1) / THREADS;
     static constexpr int B_SUBS = (BK / 4) * (BN / 8);     // 4k x 8n blocks
     static constexpr int B_PER_THREAD = (B_SUBS + THREADS - 1) / THREADS;
+    static constexpr int BT_VECS = BN * BK / 8;            // transposed W: 16-byte vectors
+    static constexpr int BT_PER_THREAD = (BT_VECS + THREADS - 1) / THREADS;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be 16-aligned");
     static_assert(BK % 32 == 0, "K block must hold whole MFMA steps");
 };
@@ -57,15 +59,17 @@ constexpr int lds_bytes()
     return T::LDS_BYTES + (TopLevelInLds<T, CPS>::value ? T::WAVES * T::FM * T::FN * 64 * 16 : 0);
 }
 
-template <class T>
+// WT: W is given transposed ([N][K], K contiguous); its rows then load like
+// the rows of X and go to LDS unchanged.
+template <class T, bool WT>
 struct Prefetch {
     uint4 a[T::A_PER_THREAD];
-    uint4 b[T::B_PER_THREAD][4];
+    uint4 b[WT ? T::BT_PER_THREAD : T::B_PER_THREAD][WT ? 1 : 4];
 };
 
 // Global -> registers for one K block [kb, kb+BK) clipped to the chunk end ce.
-template <class T>
-__device__ __forceinline__ void load_block(Prefetch<T>& pf, const GemmArgs& g,
+template <class T, bool WT>
+__device__ __forceinline__ void load_block(Prefetch<T, WT>& pf, const GemmArgs& g,
                                            int row0, int col0, int kb, int ce, int tid)
 {
 #pragma unroll
@@ -79,6 +83,21 @@ __device__ __forceinline__ void load_block(Prefetch<T>& pf, const GemmArgs& g,
                 val = *reinterpret_cast<const uint4*>(g.X + (size_t)grow * g.ldx + gk);
         }
         pf.a[i] = val;
+    }
+    if constexpr (WT) {
+#pragma unroll
+        for (int i = 0; i < T::BT_PER_THREAD; ++i) {
+            const int v = tid + i * T::THREADS;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (v < T::BT_VECS) {
+                const int n = v / (T::BK / 8), kv = v % (T::BK / 8);
+                const int gn = col0 + n, gk = kb + 8 * kv;
+                if (gn < g.N && gk < ce)
+                    val = *reinterpret_cast<const uint4*>(g.W + (size_t)gn * g.ldw + gk);
+            }
+            pf.b[i][0] = val;
+        }
+        return;
     }
 #pragma unroll
     for (int i = 0; i < T::B_PER_THREAD; ++i) {
@@ -98,8 +117,8 @@ __device__ __forceinline__ void load_block(Prefetch<T>& pf, const GemmArgs& g,
 
 // Registers -> LDS stage.  A is copied as is; each 4k x 8n block of B is
 // transposed to 8 rows (one per n) of 4 consecutive k.
-template <class T>
-__device__ __forceinline__ void store_block(const Prefetch<T>& pf, uint16_t* stage, int tid)
+template <class T, bool WT>
+__device__ __forceinline__ void store_block(const Prefetch<T, WT>& pf, uint16_t* stage, int tid)
 {
     uint16_t* sA = stage;
     uint16_t* sB = stage + T::A_ELEMS;
@@ -110,6 +129,17 @@ __device__ __forceinline__ void store_block(const Prefetch<T>& pf, uint16_t* sta
             const int r = v / (T::BK / 8), kv = v % (T::BK / 8);
             *reinterpret_cast<uint4*>(sA + r * T::LDK + 8 * kv) = pf.a[i];
         }
+    }
+    if constexpr (WT) {
+#pragma unroll
+        for (int i = 0; i < T::BT_PER_THREAD; ++i) {
+            const int v = tid + i * T::THREADS;
+            if (v < T::BT_VECS) {
+                const int n = v / (T::BK / 8), kv = v % (T::BK / 8);
+                *reinterpret_cast<uint4*>(sB + n * T::LDK + 8 * kv) = pf.b[i][0];
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int i = 0; i < T::B_PER_THREAD; ++i) {
@@ -169,7 +199,7 @@ __device__ __forceinline__ void mma_block(f32x4 (&acc)[T::FM][T::FN], const uint
     }
 }
 
-template <class T, int CPS, int EPI>
+template <class T, int CPS, int EPI, bool WT>
 __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -201,10 +231,10 @@ __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
     f32x4 stk[NSTK][T::FM][T::FN];
     f32x4* lds_top = reinterpret_cast<f32x4*>(smem + 2 * T::STAGE_ELEMS) +
                      wave * (T::FM * T::FN * 64) + lane;
-    Prefetch<T> pf;
+    Prefetch<T, WT> pf;
 
-    load_block<T>(pf, g, row0, col0, kslice, kslice + g.Kc, tid);
-    store_block<T>(pf, smem, tid);
+    load_block<T, WT>(pf, g, row0, col0, kslice, kslice + g.Kc, tid);
+    store_block<T, WT>(pf, smem, tid);
     __syncthreads();
 
 #pragma unroll
@@ -225,7 +255,7 @@ __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
                 const int nc = (b + 1 < nb) ? c : c + 1;
                 const int nbi = (b + 1 < nb) ? b + 1 : 0;
                 const int nbeg = kslice + nc * g.Kc;
-                load_block<T>(pf, g, row0, col0, nbeg + nbi * T::BK, nbeg + g.Kc, tid);
+                load_block<T, WT>(pf, g, row0, col0, nbeg + nbi * T::BK, nbeg + g.Kc, tid);
             }
             const int kb = cbeg + b * T::BK;
             int nks = (cend - kb + 31) / 32;
@@ -236,7 +266,7 @@ __global__ __launch_bounds__(T::THREADS) void slice_gemm_kernel(GemmArgs g)
             else if (fm_act > 0 && fn_act > 0)
                 mma_block<T, false>(acc, stage, nks, wm, wn, lane, fm_act, fn_act);
             if (more)
-                store_block<T>(pf, smem + ((t + 1) & 1) * T::STAGE_ELEMS, tid);
+                store_block<T, WT>(pf, smem + ((t + 1) & 1) * T::STAGE_ELEMS, tid);
             __syncthreads();
         }
         fold_chunk<T::FM, T::FN, LOG, REG_LEVELS, NSTK>(c, acc, stk, lds_top);
@@ -312,10 +342,10 @@ __global__ __launch_bounds__(256) void epilogue_only_kernel(GemmArgs g)
 
 // ---------------------------------------------------------------- launches
 
-template <class T, int CPS, int EPI>
+template <class T, int CPS, int EPI, bool WT>
 static hipError_t launch_t(const GemmArgs& g, hipStream_t s)
 {
-    auto fn = slice_gemm_kernel<T, CPS, EPI>;
+    auto fn = slice_gemm_kernel<T, CPS, EPI, WT>;
     constexpr int lds = lds_bytes<T, CPS>();
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -326,18 +356,18 @@ static hipError_t launch_t(const GemmArgs& g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <class T, int EPI>
+template <class T, int EPI, bool WT>
 static hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (cps) {
-    case 1: return launch_t<T, 1, EPI>(g, s);
-    case 2: return launch_t<T, 2, EPI>(g, s);
-    case 4: return launch_t<T, 4, EPI>(g, s);
+    case 1: return launch_t<T, 1, EPI, WT>(g, s);
+    case 2: return launch_t<T, 2, EPI, WT>(g, s);
+    case 4: return launch_t<T, 4, EPI, WT>(g, s);
     case 8:
         if constexpr (EPI == EPI_COMBINE)  // a single slice never needs a combine
             return hipErrorInvalidValue;
         else
-            return launch_t<T, 8, EPI>(g, s);
+            return launch_t<T, 8, EPI, WT>(g, s);
     }
     return hipErrorInvalidValue;
 }
@@ -345,10 +375,18 @@ static hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 template <int EPI>
 static hipError_t launch_tile(int tile, const GemmArgs& g, int cps, hipStream_t s)
 {
+    if (g.wt) {
+        switch (tile) {
+        case TILE_S16: return launch_cps<TileS16, EPI, true>(g, cps, s);
+        case TILE_M64: return launch_cps<TileM64, EPI, true>(g, cps, s);
+        case TILE_L128: return launch_cps<TileL128, EPI, true>(g, cps, s);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (tile) {
-    case TILE_S16: return launch_cps<TileS16, EPI>(g, cps, s);
-    case TILE_M64: return launch_cps<TileM64, EPI>(g, cps, s);
-    case TILE_L128: return launch_cps<TileL128, EPI>(g, cps, s);
+    case TILE_S16: return launch_cps<TileS16, EPI, false>(g, cps, s);
+    case TILE_M64: return launch_cps<TileM64, EPI, false>(g, cps, s);
+    case TILE_L128: return launch_cps<TileL128, EPI, false>(g, cps, s);
     }
     return hipErrorInvalidValue;
 }

@@ -14,7 +14,9 @@
 //    ds_read_b128 per MFMA operand;
 //  * B (W, N-contiguous) is stored [k][n] as loaded and read with
 //    ds_read_b64_tr_b16, which hands each lane four consecutive k of one
-//    column; two such reads form one MFMA operand;
+//    column; two such reads form one MFMA operand.  A W given transposed
+//    ([N][K], the layout of a linear layer's weight) is stored [n][k] and
+//    read like A;
 //  * both layouts XOR-swizzle 16-byte chunks within a row so that the
 //    fragment reads spread over the LDS banks (the DMA writes each wave's
 //    1 KiB contiguously, so the swizzle is chosen by which global chunk
@@ -104,16 +106,19 @@ __device__ __forceinline__ void wait_lgkmcnt0()
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Scheduling hint for one k step: alternate its 16 MFMAs with the 12 LDS
-// reads (4 A, 8 transposed B) of the next k step.
+// Scheduling hint for one k step: alternate its 16 MFMAs with the LDS
+// reads of the next k step (4 A and 8 transposed B reads, or 4 + 4 when W
+// comes transposed).
+template <bool WT>
 __device__ __forceinline__ void interleave_reads_with_mfma()
 {
+    constexpr int READS = WT ? 8 : 12;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < READS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 - READS, 0);
 }
 
 // Swizzle of the B tile: k-row k keeps its 16 chunks of 8 columns, with the
@@ -137,6 +142,20 @@ __device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfr)[FN], 
         const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         bfr[fn] = __builtin_bit_cast(bf16x8, both);
     }
+}
+
+// Fragments of one k step when W comes transposed: B is stored [n][k] like
+// A and read the same way, one 16-byte read per operand.
+__device__ __forceinline__ void load_frags_wt(bf16x8 (&af)[FM], bf16x8 (&bfr)[FN],
+                                              const uint8_t* st, uint32_t a_addr,
+                                              uint32_t bt_addr)
+{
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *reinterpret_cast<const bf16x8*>(st + a_addr + fm * 16 * 8 * 16);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(st + A_BYTES + bt_addr + fn * 16 * 8 * 16);
 }
 
 __device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af)[FM],
@@ -261,7 +280,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], c
     }
 }
 
-template <int STAGES, int CPS, int EPI, bool PARK>
+template <int STAGES, int CPS, int EPI, bool PARK, bool WT>
 __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -282,11 +301,16 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     // Buffer descriptors over the tile's rows of X and columns of W.  Reads
     // past the record count return zeros (rows >= M, the last row's
     // columns >= N).
+    // With W transposed the descriptor covers the tile's rows of W (columns
+    // >= N read zeros, like rows >= M of X).
     const int rows_valid = (g.M - row0) < BM ? (g.M - row0) : BM;
+    const int cols_valid = (g.N - col0) < BN ? (g.N - col0) : BN;
     const uint16_t* xa = g.X + (size_t)row0 * g.ldx;
-    const uint16_t* wb = g.W + col0;
+    const uint16_t* wb = WT ? g.W + (size_t)col0 * g.ldw : g.W + col0;
     const uint32_t a_bytes = (uint32_t)(((size_t)(rows_valid - 1) * g.ldx + g.K) * 2);
-    const uint32_t b_bytes = (uint32_t)(((size_t)(g.K - 1) * g.ldw + (g.N - col0)) * 2);
+    const uint32_t b_bytes =
+        WT ? (uint32_t)(((size_t)(cols_valid - 1) * g.ldw + g.K) * 2)
+           : (uint32_t)(((size_t)(g.K - 1) * g.ldw + (g.N - col0)) * 2);
     const i32x4 ra = buffer_desc(xa, a_bytes);
     const i32x4 rb = buffer_desc(wb, b_bytes);
     const uint32_t smem_lds = (uint32_t)(uintptr_t)((DETRED_LDS uint8_t*)smem);
@@ -298,8 +322,13 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
         const int s = (wave * LOADS + i) * 64 + lane;       // 16-byte slot in the stage
         const int r = s >> 3, ca = (s & 7) ^ (r & 7);       // A: row r, k-chunk ca
         offa[i] = (uint32_t)((r * g.ldx + 8 * ca) * 2);
-        const int k = s >> 4, cb = (s & 15) ^ b_swz(k);     // B: k-row k, n-chunk cb
-        offb[i] = (uint32_t)((k * g.ldw + 8 * cb) * 2);
+        if (WT) {
+            const int n = s >> 3, cn = (s & 7) ^ (n & 7);  // B: row n, k-chunk cn
+            offb[i] = (uint32_t)((n * g.ldw + 8 * cn) * 2);
+        } else {
+            const int k = s >> 4, cb = (s & 15) ^ b_swz(k); // B: k-row k, n-chunk cb
+            offb[i] = (uint32_t)((k * g.ldw + 8 * cb) * 2);
+        }
     }
 
     const int kslice = tc.z * CPS * g.Kc;
@@ -319,7 +348,8 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             dma16(st + i * 1024, offa[i] + (uint32_t)kb * 2, ra);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-            dma16(st + A_BYTES + i * 1024, offb[i] + (uint32_t)kb * ldw_bytes, rb);
+            dma16(st + A_BYTES + i * 1024,
+                  offb[i] + (WT ? (uint32_t)kb * 2 : (uint32_t)kb * ldw_bytes), rb);
     };
     constexpr int LOADS_PER_ISSUE = 2 * LOADS;
 
@@ -333,6 +363,13 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     for (int ks = 0; ks < KSTEPS; ++ks) {
         const int r = wm * TM + j;
         a_addr[ks] = (uint32_t)((r * 8 + ((4 * ks + gq) ^ (lane & 7))) * 16);
+    }
+    // transposed W: row n = wn*64 + fn*16 + lane%16, k-chunk as for A
+    uint32_t bt_addr[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int n = wn * TN + j;
+        bt_addr[ks] = (uint32_t)((n * 8 + ((4 * ks + gq) ^ (lane & 7))) * 16);
     }
     uint32_t b_addr[FN];
 #pragma unroll
@@ -370,8 +407,14 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     __builtin_amdgcn_sched_barrier(0);
 
     bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    auto frags = [&](bf16x8(&af)[FM], bf16x8(&bfr)[FN], const uint8_t* st, int ks) {
+        if constexpr (WT)
+            load_frags_wt(af, bfr, st, a_addr[ks], bt_addr[ks]);
+        else
+            load_frags(af, bfr, st, a_addr[ks], b_addr, ks);
+    };
     if (active)
-        load_frags(fa0, fb0, smem, a_addr[0], b_addr, 0);
+        frags(fa0, fb0, smem, 0);
 
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
@@ -389,9 +432,9 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             const uint8_t* st_next = smem + ((t + 1) % STAGES) * STAGE_BYTES;
             __builtin_amdgcn_sched_barrier(0);
             if (active) {
-                load_frags(fa1, fb1, st, a_addr[1], b_addr, 1);
+                frags(fa1, fb1, st, 1);
                 mma_step(acc, fa0, fb0);
-                interleave_reads_with_mfma();
+                interleave_reads_with_mfma<WT>();
             }
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkmcnt0();
@@ -407,11 +450,11 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             if (active) {
                 // the next block's reads are harmless after the last block
                 if (two_steps) {
-                    load_frags(fa0, fb0, st_next, a_addr[0], b_addr, 0);
+                    frags(fa0, fb0, st_next, 0);
                     mma_step(acc, fa1, fb1);
-                    interleave_reads_with_mfma();
+                    interleave_reads_with_mfma<WT>();
                 } else {
-                    load_frags(fa0, fb0, st_next, a_addr[0], b_addr, 0);
+                    frags(fa0, fb0, st_next, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -450,12 +493,12 @@ struct Stages {
     static constexpr int value = park ? 2 : DETRED_LDS_STAGES;
 };
 
-template <int CPS, int EPI>
+template <int CPS, int EPI, bool WT>
 hipError_t launch(const GemmArgs& g, hipStream_t s)
 {
     constexpr int ST = Stages<CPS>::value;
     constexpr bool PK = Stages<CPS>::park;
-    auto fn = lds_gemm_kernel<ST, CPS, EPI, PK>;
+    auto fn = lds_gemm_kernel<ST, CPS, EPI, PK, WT>;
     constexpr int bytes = ST * STAGE_BYTES + (PK ? PARK_BYTES : 0) + SCRATCH_BYTES + 16;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -466,20 +509,26 @@ hipError_t launch(const GemmArgs& g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool WT>
 hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (cps) {
-    case 1: return launch<1, EPI>(g, s);
-    case 2: return launch<2, EPI>(g, s);
-    case 4: return launch<4, EPI>(g, s);
+    case 1: return launch<1, EPI, WT>(g, s);
+    case 2: return launch<2, EPI, WT>(g, s);
+    case 4: return launch<4, EPI, WT>(g, s);
     case 8:
         if constexpr (EPI == EPI_COMBINE)
             return hipErrorInvalidValue;
         else
-            return launch<8, EPI>(g, s);
+            return launch<8, EPI, WT>(g, s);
     }
     return hipErrorInvalidValue;
+}
+
+template <int EPI>
+hipError_t launch_layout(const GemmArgs& g, int cps, hipStream_t s)
+{
+    return g.wt ? launch_cps<EPI, true>(g, cps, s) : launch_cps<EPI, false>(g, cps, s);
 }
 
 }  // namespace lds
@@ -493,7 +542,8 @@ bool lds_engine_supports(const GemmArgs& g, int cps)
     if (g.Kc % 32 != 0)
         return false;
     const size_t xbytes = ((size_t)(lds::BM - 1) * g.ldx + g.K) * 2;
-    const size_t wbytes = ((size_t)g.K * g.ldw) * 2;
+    const size_t wbytes = g.wt ? ((size_t)(lds::BN - 1) * g.ldw + g.K) * 2
+                               : ((size_t)g.K * g.ldw) * 2;
     // output rows of the tile (Y at ldy, partial planes at N, C at ldc)
     // likewise
     size_t ld = (size_t)(g.ldy > g.N ? g.ldy : g.N);
@@ -506,9 +556,9 @@ bool lds_engine_supports(const GemmArgs& g, int cps)
 hipError_t launch_lds_gemm(int epi, const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (epi) {
-    case EPI_STORE: return lds::launch_cps<EPI_STORE>(g, cps, s);
-    case EPI_COMBINE: return lds::launch_cps<EPI_COMBINE>(g, cps, s);
-    case EPI_ATOMIC: return lds::launch_cps<EPI_ATOMIC>(g, cps, s);
+    case EPI_STORE: return lds::launch_layout<EPI_STORE>(g, cps, s);
+    case EPI_COMBINE: return lds::launch_layout<EPI_COMBINE>(g, cps, s);
+    case EPI_ATOMIC: return lds::launch_layout<EPI_ATOMIC>(g, cps, s);
     }
     return hipErrorInvalidValue;
 }

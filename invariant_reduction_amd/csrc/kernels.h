@@ -14,6 +14,10 @@ struct GemmArgs {
     long ldx;
     const uint16_t* W;
     long ldw;
+    // wt == 0: W is [K][N] (element (k, n) at W[k*ldw + n]); wt == 1: W is
+    // given transposed, [N][K] (element (k, n) at W[n*ldw + k]).  The
+    // products and their order are the same, so are the bits.
+    int wt;
     float* Y;             // output (EPI_STORE: slice z writes Y + z*out_z_stride)
     long ldy;
     long out_z_stride;

@@ -37,6 +37,9 @@ SIGNATURES = {
     "det_splitk_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "det_splitk_addmm": ([_P, _I, _P, _I, _P, _I, _F, _F, _P, _I, _I, _I, _I, _I, _I, _P, _Z,
                           _P], _I),
+    "det_splitk_gemm_wt": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "det_splitk_addmm_wt": ([_P, _I, _P, _I, _P, _I, _F, _F, _P, _I, _I, _I, _I, _I, _I, _P, _Z,
+                             _P], _I),
     "det_lora_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "det_lora_forward": ([_P, _I, _P, _I, _P, _I, _P, _I, _F, _P, _I, _I, _I, _I, _I, _P, _Z,
                           _P], _I),
@@ -140,6 +143,23 @@ def _mat(t, dtypes, name):
     return ctypes.c_void_p(t.data_ptr()), int(ld)
 
 
+def _weight(W):
+    """The right operand of a product: a row-major [K, N] matrix, or a
+    [K, N] view of a row-major [N, K] matrix (W = Wt.t(), as a linear
+    layer's weight is used).  Returns (pointer, leading dimension,
+    transposed)."""
+    if not isinstance(W, torch.Tensor):
+        raise TypeError("W must be a torch tensor")
+    if W.dim() == 2 and W.shape[0] > 1 and W.shape[1] > 1 and W.stride(0) == 1 and W.stride(1) != 1:
+        if W.dtype not in _BF16_TYPES:
+            raise TypeError("W has dtype %s, expected one of %s" % (W.dtype, _BF16_TYPES))
+        if not W.is_cuda:
+            raise ValueError("W must be a GPU tensor")
+        return ctypes.c_void_p(W.data_ptr()), int(W.stride(1)), True
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    return pw, ldw, False
+
+
 def policy(N, K):
     """The locked policy for (N, K): dict with chunks, chunk_k, tile_m,
     tile_n, default_split."""
@@ -199,23 +219,26 @@ def _gemm_dims(X, W, Y):
 
 @_entry
 def det_splitk_gemm(X, W, Y, split_k=0, ws=None, stream=None):
-    """Y[M,N] (fp32) = X[M,K] W[K,N] (bf16) with the fixed chunk tree."""
+    """Y[M,N] (fp32) = X[M,K] W[K,N] (bf16) with the fixed chunk tree.  W may
+    be the transpose view of a row-major [N, K] weight (det_splitk_gemm_wt;
+    same bits)."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
-    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    pw, ldw, wt = _weight(W)
     py, ldy = _mat(Y, (torch.float32,), "Y")
     M, N, K = _gemm_dims(X, W, Y)
     pws, nws = _ws(ws)
-    return "det_splitk_gemm", (px, ldx, pw, ldw, py, ldy, M, N, K, split_k, pws, nws,
-                                 _stream(stream))
+    return ("det_splitk_gemm_wt" if wt else "det_splitk_gemm"), (
+        px, ldx, pw, ldw, py, ldy, M, N, K, split_k, pws, nws, _stream(stream))
 
 
 @_entry
 def det_splitk_addmm(X, W, Y, C=None, alpha=1.0, beta=1.0, split_k=0, ws=None, stream=None):
     """Y = beta*C + alpha*(X W) with the canonical product; Y fp32 or bf16
     (bf16/int16/uint16 dtype = bf16 output).  C: None, a length-N fp32 bias
-    (broadcast to every row) or an fp32 [M, N] matrix."""
+    (broadcast to every row) or an fp32 [M, N] matrix.  W may be the
+    transpose view of a row-major [N, K] weight (det_splitk_addmm_wt)."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
-    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    pw, ldw, wt = _weight(W)
     out_bf16 = Y.dtype in _BF16_TYPES
     py, ldy = _mat(Y, _BF16_TYPES + (torch.float32,), "Y")
     M, N, K = _gemm_dims(X, W, Y)
@@ -230,9 +253,9 @@ def det_splitk_addmm(X, W, Y, C=None, alpha=1.0, beta=1.0, split_k=0, ws=None, s
         if tuple(C.shape) != (M, N):
             raise ValueError("C must be [M, N]")
     pws, nws = _ws(ws)
-    return "det_splitk_addmm", (px, ldx, pw, ldw, pc, ldc, float(alpha), float(beta), py, ldy,
-                                  BF16 if out_bf16 else F32, M, N, K, split_k, pws, nws,
-                                  _stream(stream))
+    return ("det_splitk_addmm_wt" if wt else "det_splitk_addmm"), (
+        px, ldx, pw, ldw, pc, ldc, float(alpha), float(beta), py, ldy, BF16 if out_bf16 else F32,
+        M, N, K, split_k, pws, nws, _stream(stream))
 
 
 def det_lora_workspace_bytes(M, N, K, r):

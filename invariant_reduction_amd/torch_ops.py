@@ -15,8 +15,10 @@ The products round the binary32 result to bf16 once, as torch's bf16 mm
 does.  A call outside what the kernels cover (another dtype, another
 dimension, shapes or alignments the C ABI rejects) raises
 NotImplementedError instead of falling back to a kernel whose result could
-depend on the batch.  A second operand that is not row-major (F.linear
-passes W.t()) is copied to row-major first.  Operators on CPU tensors are
+depend on the batch.  A second operand that is the transpose view of a
+row-major weight (F.linear passes W.t()) goes to the transposed-weight
+kernels as it is; any other second operand that is not row-major is copied
+to row-major first.  Operators on CPU tensors are
 not affected.  Argument marshalling only: every result comes from
 libdetred's HIP kernels.
 """
@@ -37,6 +39,16 @@ def _row_major(t):
     return t.contiguous()
 
 
+def _right_operand(b):
+    """b as the library takes it: a [K, N] view of a row-major [N, K] weight
+    (linear layers call addmm with weight.t()) goes as it is, to the
+    transposed-weight kernels; anything else as a row-major matrix."""
+    if b.dim() == 2 and b.shape[0] > 1 and b.shape[1] > 1 and b.stride(0) == 1 and \
+            b.stride(1) % 8 == 0 and b.data_ptr() % 16 == 0:
+        return b
+    return _row_major(b)
+
+
 def _check_mm(a, b):
     if a.dtype not in _BF16 or b.dtype not in _BF16:
         raise NotImplementedError("batch-invariant mm covers bf16 operands, got %s x %s" % (a.dtype, b.dtype))
@@ -46,7 +58,7 @@ def _check_mm(a, b):
     N = b.shape[1]
     if K % 8 or N % 8:
         raise NotImplementedError("batch-invariant mm needs K and N multiples of 8 (K=%d, N=%d)" % (K, N))
-    return _row_major(a), _row_major(b), M, N, K
+    return _row_major(a), _right_operand(b), M, N, K
 
 
 def _product(a, b, c, alpha, beta):

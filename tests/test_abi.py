@@ -114,6 +114,31 @@ def test_det_splitk_rejects(kw, status):
     assert call_det(**kw) == status
 
 
+def test_transposed_weight_entry_points_reject():
+    L = detred.lib()
+    f = ctypes.c_float
+    # det_splitk_gemm_wt(X, ldx, Wt, ldwt, Y, ldy, M, N, K, S, ws, ws_bytes, s): Wt is [N, K]
+    g = lambda **kw: [kw.get("X", A16), 512, kw.get("W", A16b), kw.get("ldw", 512), A16c,
+                      kw.get("ldy", 16), 16, kw.get("N", 16), 512, kw.get("S", 1), None, 0, None]
+    assert L.det_splitk_gemm_wt(*g(ldw=16)) == detred.EINVAL       # ldwt < K (ldw >= N is not enough)
+    assert L.det_splitk_gemm_wt(*g(ldw=500)) == detred.EINVAL      # ldwt < K
+    assert L.det_splitk_gemm_wt(*g(ldw=516)) == detred.EINVAL      # ldwt % 8 != 0
+    assert L.det_splitk_gemm_wt(*g(W=MIS)) == detred.EINVAL
+    assert L.det_splitk_gemm_wt(*g(W=None)) == detred.EINVAL
+    assert L.det_splitk_gemm_wt(*g(S=3)) == detred.EUNSUPPORTED
+    assert L.det_splitk_gemm_wt(*g(S=8)) == detred.EWORKSPACE
+    assert L.det_splitk_gemm_wt(*g(N=12, ldy=16)) == detred.EUNSUPPORTED
+    a = g(X=None, W=None)
+    a[6] = 0                                                      # M == 0
+    assert L.det_splitk_gemm_wt(*a) == detred.OK
+    # det_splitk_addmm_wt(X, ldx, Wt, ldwt, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K, S, ws, ws_bytes, s)
+    am = lambda **kw: [A16, 512, A16b, kw.get("ldw", 512), A16c, kw.get("ldc", 16), f(1.0), f(1.0),
+                       A16, 16, kw.get("dt", detred.F32), 16, 16, 512, 1, None, 0, None]
+    assert L.det_splitk_addmm_wt(*am(ldw=16)) == detred.EINVAL
+    assert L.det_splitk_addmm_wt(*am(dt=2)) == detred.EINVAL
+    assert L.det_splitk_addmm_wt(*am(ldc=8)) == detred.EINVAL
+
+
 def test_empty_problem_launches_nothing():
     # M == 0 or N == 0: OK without touching the (null) pointers
     assert call_det(X=None, W=None, Y=None, M=0) == detred.OK
