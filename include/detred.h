@@ -193,9 +193,9 @@ int det_splitk_addmm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt
 
 /*
  * Workspace of det_lora_forward for an M x N layer output with input width K
- * and LoRA rank r: the fp32 base product, the fp32 shrink output, its bf16
- * cast and the split-K workspaces of the base product and the shrink, each
- * 256-byte aligned.  0 for invalid arguments.
+ * and LoRA rank r: the fp32 base product, the bf16 shrink output and the
+ * split-K workspaces of the base product and the shrink, each 256-byte
+ * aligned.  0 for invalid arguments.
  */
 size_t det_lora_workspace_bytes(int M, int N, int K, int r);
 
@@ -204,14 +204,16 @@ size_t det_lora_workspace_bytes(int M, int N, int K, int r);
  * (split-K paper, Highlights and Q&A: the base product, the shrink X*A and
  * the expand of its bf16 cast by B):
  *   base = det_splitk_gemm(X, W)              fp32 [M,N], policy split;
- *   z    = det_splitk_gemm(X, A)              fp32 [M,r], policy split (8);
- *   zb   = detred_f32_to_bf16(z)              bf16 [M,r];
+ *   zb   = det_splitk_addmm(X, A, no C, alpha = 1, bf16 output)
+ *                                             bf16 [M,r], policy split (8):
+ *          the bits of detred_f32_to_bf16(det_splitk_gemm(X, A)), the
+ *          rounding done in the shrink's own epilogue;
  *   Y    = det_splitk_addmm(zb, B, C = base, alpha = scale, beta = 1,
  *                           bf16 output)      bf16 [M,N]
  * i.e. Y = bf16(base + scale*(zb*B)).  X [M,K] ld ldx, W [K,N] ld ldw,
  * A [K,r] ld lda, B [r,N] ld ldb, all bf16; Y bf16 ld ldy.  r % 8 == 0,
  * K % 8 == 0, N % 8 == 0.  ws: det_lora_workspace_bytes(M,N,K,r) bytes,
- * 256-byte aligned, zeroed once with detred_workspace_init.  Four launches
+ * 256-byte aligned, zeroed once with detred_workspace_init.  Three launches
  * on s.  The bits of Y do not depend on M.
  */
 int det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W, int ldw,

@@ -268,7 +268,7 @@ int check_epilogue(const float* C, int ldc, int N, int y_dtype)
 
 // Byte layout of the det_lora_forward workspace.
 struct LoraLayout {
-    size_t base, z, zb, ws_base, ws_z, total;
+    size_t base, zb, ws_base, ws_z, total;
     size_t ws_base_bytes, ws_z_bytes;
     int s_base, s_z;
 };
@@ -281,8 +281,7 @@ LoraLayout lora_layout(int M, int N, int K, int r)
     l.ws_base_bytes = detred_gemm_workspace_bytes(M, N, K, l.s_base);
     l.ws_z_bytes = detred_gemm_workspace_bytes(M, r, K, l.s_z);
     l.base = 0;
-    l.z = l.base + round_up((size_t)M * N * sizeof(float), 256);
-    l.zb = l.z + round_up((size_t)M * r * sizeof(float), 256);
+    l.zb = l.base + round_up((size_t)M * N * sizeof(float), 256);
     l.ws_base = l.zb + round_up((size_t)M * r * sizeof(uint16_t), 256);
     l.ws_z = l.ws_base + round_up(l.ws_base_bytes, 256);
     l.total = l.ws_z + round_up(l.ws_z_bytes, 256);
@@ -393,13 +392,12 @@ int det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
         return DETRED_EWORKSPACE;
     char* w = (char*)ws;
     float* base = (float*)(w + l.base);
-    float* z = (float*)(w + l.z);
     uint16_t* zb = (uint16_t*)(w + l.zb);
     const Policy pb = plan(M, N, K), pz = plan(M, r, K), pe = plan(M, N, r);
     // every check before the first launch
     int st;
     if ((st = check_gemm(X, ldx, W, ldw, base, N, M, N, K)) != DETRED_OK ||
-        (st = check_gemm(X, ldx, A, lda, z, r, M, r, K)) != DETRED_OK ||
+        (st = check_gemm(X, ldx, A, lda, (const float*)zb, r, M, r, K)) != DETRED_OK ||
         (st = check_gemm(zb, r, B, ldb, (const float*)Y, ldy, M, N, r)) != DETRED_OK ||
         (st = check_det(pb, M, N, K, l.s_base, w + l.ws_base, l.ws_base_bytes)) != DETRED_OK ||
         (st = check_det(pz, M, r, K, l.s_z, w + l.ws_z, l.ws_z_bytes)) != DETRED_OK)
@@ -408,11 +406,13 @@ int det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
     const GemmArgs gb = make_args(pb, X, ldx, W, ldw, base, N, M, N, K, l.s_base);
     if ((st = run_det(pb, gb, l.s_base, w + l.ws_base, l.ws_base_bytes, hs)) != DETRED_OK)
         return st;
-    const GemmArgs gz = make_args(pz, X, ldx, A, lda, z, r, M, r, K, l.s_z);
+    // the shrink rounds its final values to bf16 in its own epilogue (alpha
+    // = 1, no C): the bits of casting its fp32 result, one launch fewer
+    GemmArgs gz = make_args(pz, X, ldx, A, lda, (float*)zb, r, M, r, K, l.s_z);
+    gz.epi = 1;
+    gz.out_bf16 = 1;
     if ((st = run_det(pz, gz, l.s_z, w + l.ws_z, l.ws_z_bytes, hs)) != DETRED_OK)
         return st;
-    if (launch_cast_bf16(z, zb, (size_t)M * r, hs) != hipSuccess)
-        return DETRED_EHIP;
     GemmArgs ge = make_args(pe, zb, r, B, ldb, (float*)Y, ldy, M, N, r, 1);
     ge.epi = 1;
     ge.C = base;

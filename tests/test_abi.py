@@ -204,9 +204,9 @@ def test_addmm_lora_and_bf16_rmsnorm_reject():
     assert L.det_lora_forward(*lora(X=MIS)) == detred.EINVAL
     assert L.det_lora_workspace_bytes(16, 64, 512, 0) == 0
     need = L.det_lora_workspace_bytes(16, 64, 512, 16)
-    # base [16,64] + shrink fp32 [16,16] + its bf16 + the split-K workspaces of
+    # base [16,64] fp32 + the bf16 shrink [16,16] + the split-K workspaces of
     # the base product and the shrink (both split 8 by the policy: N <= 64)
-    assert need == 4096 + 1024 + 512 + L.detred_gemm_workspace_bytes(16, 64, 512, 8) + \
+    assert need == 4096 + 512 + L.detred_gemm_workspace_bytes(16, 64, 512, 8) + \
         L.detred_gemm_workspace_bytes(16, 16, 512, 8)
     assert L.inv_rmsnorm_bf16(A16, A16b, A16c, 4, 4100, f(1e-6), None) == detred.EUNSUPPORTED
     assert L.inv_rmsnorm_bf16(A16, None, A16c, 4, 4096, f(1e-6), None) == detred.EINVAL

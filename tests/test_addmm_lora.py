@@ -7,7 +7,7 @@ split and of M; with alpha, beta powers of two the result must equal
 det_splitk_gemm followed by the same two fp32 operations bit for bit.  A bf16
 output is the rounding of the fp32 output: both sides take that decision
 on the same binary32 value, so it is compared bit for bit through the
-oracle's own rounding.  The LoRA layer must equal its four steps run one by
+oracle's own rounding.  The LoRA layer must equal its steps run one by
 one, bit for bit, and the fp32 form of its last step must meet the oracle's
 tolerance."""
 import numpy as np
@@ -188,7 +188,7 @@ def test_lora_forward_steps_and_parity(M, N, K, r, scale, dev):
     Xd, Wd, Ad, Bd = (dev_bf16(t, dev) for t in (X, W, A, B))
     Y = torch.full((M, N), -1, dtype=torch.int16, device=dev)
     detred.det_lora_forward(Xd, Wd, Ad, Bd, Y, scale, detred.lora_workspace(M, N, K, r, dev))
-    # the four steps one by one
+    # the steps one by one, the cast of the shrink as its own call
     base = torch.empty((M, N), dtype=torch.float32, device=dev)
     detred.det_splitk_gemm(Xd, Wd, base, 0, detred.workspace(M, N, K, 0, dev))
     z = torch.empty((M, r), dtype=torch.float32, device=dev)
