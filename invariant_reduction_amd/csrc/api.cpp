@@ -129,6 +129,27 @@ GemmArgs make_args(const Policy& p, const uint16_t* X, int ldx, const uint16_t* 
     return g;
 }
 
+// Subtree roots of one-chunk slices (the tree-TP shards) on the 256x256
+// tile: it halves the operand traffic into LDS per product, and at chunks of
+// 1024 or more its longer prologue and two-pass epilogue pay off (8 shards
+// of 512x8192x8192 on MI355X: 104 -> 93 us; 1024 rows: 236 -> 192 us; with
+// chunks of 512, 4096x4096x4096 at 8 shards, the 128x128 tile stays ahead,
+// 242 vs 248 us).  Taken only where the grid still has 256 workgroups.  The
+// tile never changes the bits.
+void widen_for_roots(Policy& p, GemmArgs& g, int cps)
+{
+    if (p.tile != TILE_L128 || cps != 1 || p.Kc < 1024 || g.M < 256)
+        return;
+    GemmArgs w = g;
+    w.tiles_m = (g.M + 255) / 256;
+    w.tiles_n = (g.N + 255) / 256;
+    if ((long)w.tiles_m * w.tiles_n * w.slices < 256 || !lds_engine_supports(TILE_L256, w, 1))
+        return;
+    p.tile = TILE_L256;
+    tile_shape(p.tile, &p.bm, &p.bn);
+    g = w;
+}
+
 // The split for split_k = 0.  The split only decides how many workgroups
 // share the chunk tree, never the bits.  Narrow outputs keep the policy's
 // split (one slice per chunk).  A wide product splits while its output tiles
@@ -447,7 +468,7 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
-    const Policy p = plan(M, N, K);
+    Policy p = plan(M, N, K);
     if (!pow2_le8(tp_shards) || tp_shards > p.P)
         return DETRED_EUNSUPPORTED;
     const int T = tp_shards;
@@ -463,6 +484,7 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     g.Y = (float*)ws;
     g.ldy = N;
     g.out_z_stride = (long)M * N;
+    widen_for_roots(p, g, p.P / T);
     hipError_t e = launch_slice_gemm(p.tile, EPI_STORE, g, p.P / T, hs);
     if (e != hipSuccess)
         return DETRED_EHIP;
@@ -485,7 +507,7 @@ int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, 
     int st = check_gemm(X, ldx, W, ldw, P, N, M, N, K);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
-    const Policy p = plan(M, N, K);
+    Policy p = plan(M, N, K);
     if (!pow2_le8(tp_shards) || tp_shards > p.P)
         return DETRED_EUNSUPPORTED;
     hipStream_t hs = (hipStream_t)s;
@@ -495,6 +517,7 @@ int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, 
     }
     GemmArgs g = make_args(p, X, ldx, W, ldw, P, N, M, N, K, tp_shards);
     g.out_z_stride = (long)M * N;
+    widen_for_roots(p, g, p.P / tp_shards);
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
 }
 
@@ -510,7 +533,7 @@ int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
     int st = check_gemm(Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
-    const Policy p = plan(M, N, K);
+    Policy p = plan(M, N, K);
     if (tp_shards > p.P)
         return DETRED_EUNSUPPORTED;
     hipStream_t hs = (hipStream_t)s;
@@ -518,6 +541,7 @@ int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
         return hip_status(launch_fill_zero(Pt, ldp, M, N, hs));
     // the shard's own K range is chunks [0, P/T) of width K/P
     GemmArgs g = make_args(p, Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, 1);
+    widen_for_roots(p, g, p.P / tp_shards);
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
 }
 

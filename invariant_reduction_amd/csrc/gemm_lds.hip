@@ -1,7 +1,8 @@
-// LDS-DMA slice GEMM engine for gfx950: the 128x128 workgroup tile used for
-// wide outputs.  Same reduction order, output values and last-arriver
-// combine as the register-staged engine (gemm_common.h); the data movement
-// differs:
+// LDS-DMA slice GEMM engine for gfx950: the wide-output workgroup tiles,
+// 128x128 (four waves of 64x64, any chunk count) and 256x256 (eight waves
+// of 128x64, one-chunk slices only: its accumulators leave no registers for
+// a subtree).  Same reduction order, output values and last-arriver combine
+// as the register-staged engine (gemm_common.h); the data movement differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
 //    STAGES K blocks of 64 in flight; the buffer descriptors' record counts
@@ -22,8 +23,8 @@
 //    1 KiB contiguously, so the swizzle is chosen by which global chunk
 //    each lane fetches);
 //  * the finished tile goes out through the stage buffers as whole 16-byte
-//    row pieces (store_tile_via_lds), with the addmm epilogue applied on the
-//    way when the call asks for it.
+//    row pieces (store_tile_via_lds; the 256x256 tile in two halves), with
+//    the addmm epilogue applied on the way when the call asks for it.
 //
 // Requires every 32-wide MFMA step to lie inside K (K % 32 == 0 when K is
 // one chunk; always true with 8 chunks), so no step needs zero padding.
@@ -38,17 +39,30 @@ namespace detred {
 
 namespace lds {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int WAVES = 4, THREADS = 256;       // 2 x 2 waves of 64 x 64
-constexpr int TM = 64, TN = 64, FM = 4, FN = 4;
+constexpr int BK = 64;
 constexpr int KSTEPS = BK / 32;
-constexpr int A_BYTES = BM * BK * 2;          // 16 KiB
-constexpr int B_BYTES = BK * BN * 2;          // 16 KiB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int LOADS = A_BYTES / (THREADS * 16);  // 16-byte loads per lane per operand
-static_assert(LOADS == B_BYTES / (THREADS * 16), "A and B take the same number of loads");
-constexpr int PARK_BYTES = WAVES * FM * FN * 64 * 16;  // one subtree level, all waves
 constexpr int BUFFER_DWORD3 = 0x00020000;     // raw buffer, 32-bit data format
+
+// Workgroup tile: WAVES_M x WAVES_N waves, each a TM x TN block of 16x16
+// MFMA tiles; a stage holds one 64-wide K block of A and of B.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct LdsTile {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LOADS = A_BYTES / (THREADS * 16);  // 16-byte loads per lane per operand
+    static constexpr int B_ROW_CHUNKS = BN / 8;              // 16-byte chunks per k-row of B
+    static constexpr int PARK_BYTES = WAVES * FM * FN * 64 * 16;  // one subtree level
+    static_assert(LOADS * THREADS * 16 == A_BYTES && LOADS * THREADS * 16 == B_BYTES,
+                  "A and B take the same whole number of loads per lane");
+};
+using Tile128 = LdsTile<128, 128, 2, 2>;
+using Tile256 = LdsTile<256, 256, 2, 4>;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -109,16 +123,18 @@ __device__ __forceinline__ void wait_lgkmcnt0()
 // Scheduling hint for one k step: alternate its 16 MFMAs with the LDS
 // reads of the next k step (4 A and 8 transposed B reads, or 4 + 4 when W
 // comes transposed).
-template <bool WT>
+template <class T, bool WT>
 __device__ __forceinline__ void interleave_reads_with_mfma()
 {
-    constexpr int READS = WT ? 8 : 12;
+    constexpr int READS = WT ? T::FM + T::FN : T::FM + 2 * T::FN;
+    constexpr int MFMAS = T::FM * T::FN;
+    static_assert(READS <= MFMAS, "one read per MFMA slot at most");
 #pragma unroll
     for (int i = 0; i < READS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 - READS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
 }
 
 // Swizzle of the B tile: k-row k keeps its 16 chunks of 8 columns, with the
@@ -128,17 +144,20 @@ __device__ __forceinline__ int b_swz(int k) { return 2 * ((k & 3) + 4 * ((k >> 3
 
 // Fragments of one k step: A as 16-byte reads, B as two transposed reads
 // (k0..k0+3 and k0+4..k0+7 of the lane's column).
-__device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfr)[FN], const uint8_t* st,
-                                           uint32_t a_addr, const uint32_t (&b_addr)[FN], int ks)
+template <class T>
+__device__ __forceinline__ void load_frags(bf16x8 (&af)[T::FM], bf16x8 (&bfr)[T::FN],
+                                           const uint8_t* st, uint32_t a_addr,
+                                           const uint32_t (&b_addr)[T::FN], int ks)
 {
+    constexpr int ROW = T::BN * 2;  // bytes per k-row of B
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < T::FM; ++fm)
         af[fm] = *reinterpret_cast<const bf16x8*>(st + a_addr + fm * 16 * 8 * 16);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        const uint8_t* pb = st + b_addr[fn] + ks * 32 * 256;
+    for (int fn = 0; fn < T::FN; ++fn) {
+        const uint8_t* pb = st + b_addr[fn] + ks * 32 * ROW;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb + 4 * 256));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb + 4 * ROW));
         const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         bfr[fn] = __builtin_bit_cast(bf16x8, both);
     }
@@ -146,156 +165,181 @@ __device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfr)[FN], 
 
 // Fragments of one k step when W comes transposed: B is stored [n][k] like
 // A and read the same way, one 16-byte read per operand.
-__device__ __forceinline__ void load_frags_wt(bf16x8 (&af)[FM], bf16x8 (&bfr)[FN],
+template <class T>
+__device__ __forceinline__ void load_frags_wt(bf16x8 (&af)[T::FM], bf16x8 (&bfr)[T::FN],
                                               const uint8_t* st, uint32_t a_addr,
                                               uint32_t bt_addr)
 {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < T::FM; ++fm)
         af[fm] = *reinterpret_cast<const bf16x8*>(st + a_addr + fm * 16 * 8 * 16);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const bf16x8*>(st + A_BYTES + bt_addr + fn * 16 * 8 * 16);
+    for (int fn = 0; fn < T::FN; ++fn)
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(st + T::A_BYTES + bt_addr + fn * 16 * 8 * 16);
 }
 
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[FM][FN], const bf16x8 (&af)[FM],
-                                         const bf16x8 (&bfr)[FN])
+template <class T>
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[T::FM][T::FN], const bf16x8 (&af)[T::FM],
+                                         const bf16x8 (&bfr)[T::FN])
 {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int fn = 0; fn < T::FN; ++fn)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0,
                                                                   0, 0);
 }
 
 // Epilogue store through LDS.  The MFMA layout gives a lane four rows of
-// one column, so direct stores are 4-byte scatters.  Instead the workgroup's
-// 128 x 128 fp32 tile is written to the (now idle) stage buffers row-major,
-// with the 16-column group of each element XORed by (row/4)%4 so that the
-// four row groups of a 16 x 16 result land in different banks; then every
-// thread stores whole 16-byte row pieces, 32 lanes per 512-byte tile row.
+// one column, so direct stores are 4-byte scatters.  Instead the
+// workgroup's fp32 tile is written to the (now idle) stage buffers
+// row-major, with the 16-column group of each element XORed by (row/4)%4 so
+// that the four row groups of a 16 x 16 result land in different banks;
+// then every thread stores whole 16-byte row pieces.  A tile larger than
+// the stage buffers goes in PASSES row halves, each written by the waves
+// that own those rows.
 // COHERENT: device-coherent (sc1) buffer stores, for partials that another
 // workgroup combines; shard roots (several planes, out_z_stride set) with
 // plain stores, as the cross-shard combine reads them next; final outputs
 // non-temporal (kept in the caches, a large output pushes out the operands
-// still being read).  Needs STAGES * STAGE_BYTES >= 64 KiB.
-template <bool COHERENT>
-__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[FM][FN], const GemmArgs& g,
-                                                   float* out, int ld, int row0, int col0,
-                                                   int wm, int wn, int lane, int tid,
+// still being read).
+template <class T, int STAGES, bool COHERENT>
+__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::FN],
+                                                   const GemmArgs& g, float* out, int ld, int row0,
+                                                   int col0, int wm, int wn, int lane, int tid,
                                                    uint8_t* smem)
 {
+    constexpr int BN = T::BN;
+    constexpr int PASSES = (T::BM * BN * 4 > STAGES * T::STAGE_BYTES) ? 2 : 1;
+    constexpr int HR = T::BM / PASSES;  // rows per pass
+    static_assert(HR * BN * 4 <= STAGES * T::STAGE_BYTES && HR % T::TM == 0,
+                  "a pass fits the stage buffers and holds whole wave rows");
     const int M = g.M, N = g.N;
     float* t = reinterpret_cast<float*>(smem);
-    __syncthreads();  // every wave is done with the stage buffers
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = wm * TM + fm * 16 + 4 * (lane >> 4) + q;
-                const int c = wn * TN + fn * 16 + (lane & 15);
-                t[r * BN + (c ^ (16 * ((r >> 2) & 3)))] = acc[fm][fn][q];
-            }
-    __syncthreads();
     // Stores (and epilogue loads of C) go through raw buffers based at the
     // tile's first element; a piece outside M x N gets an offset past the
     // record count, and the hardware drops the store (a load returns
-    // zeros), so the loops have no branch and the reads above stay batched.
+    // zeros), so the loops have no branch and the reads stay batched.
     constexpr int OOB = (int)0x80000000u;
-    // all of a thread's row pieces are read before the first store
-    constexpr int ITER = BM * BN / 4 / THREADS;
-    static_assert(ITER * THREADS * 4 == BM * BN, "whole float4 pieces per thread");
-    u32x4 val[ITER];
+    // A thread's row pieces of a pass are read in groups of GROUP, each
+    // group before its first store: the whole pass for a one-pass tile; 8
+    // at a time when the other half's accumulators are still live.
+    constexpr int ITER = HR * BN / 4 / T::THREADS;
+    constexpr int GROUP = PASSES > 1 ? 8 : ITER;
+    static_assert(ITER * T::THREADS * 4 == HR * BN && ITER % GROUP == 0,
+                  "whole float4 pieces per thread, whole groups");
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int v = tid + i * THREADS;
-        const int r = v / (BN / 4), c4 = v % (BN / 4);
-        val[i] = *reinterpret_cast<const u32x4*>(t + r * BN + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
-    }
-    if (COHERENT || !g.epi) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            out + (size_t)row0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
-        auto put = [&](auto policy) {
+    for (int h = 0; h < PASSES; ++h) {
+        __syncthreads();  // every wave is done with the stage buffers
+        if (wm * T::TM / HR == h) {
 #pragma unroll
-            for (int i = 0; i < ITER; ++i) {
-                const int v = tid + i * THREADS;
+            for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < T::FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = wm * T::TM - h * HR + fm * 16 + 4 * (lane >> 4) + q;
+                        const int c = wn * T::TN + fn * 16 + (lane & 15);
+                        t[r * BN + (c ^ (16 * ((r >> 2) & 3)))] = acc[fm][fn][q];
+                    }
+        }
+        __syncthreads();
+        const int prow0 = row0 + h * HR;  // first output row of this pass
+#pragma unroll
+        for (int i0 = 0; i0 < ITER; i0 += GROUP) {
+            u32x4 val[GROUP];
+#pragma unroll
+            for (int i = 0; i < GROUP; ++i) {
+                const int v = tid + (i0 + i) * T::THREADS;
                 const int r = v / (BN / 4), c4 = v % (BN / 4);
-                const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
-                const int off = in ? (r * ld + 4 * c4) * 4 : OOB;
-                __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, decltype(policy)::value);
+                val[i] = *reinterpret_cast<const u32x4*>(t + r * BN + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
             }
-        };
-        if (COHERENT)
-            put(std::integral_constant<int, CPOL_SC1>());
-        else if (g.out_z_stride)
-            // shard roots: the cross-shard combine reads them next
-            put(std::integral_constant<int, 0>());
-        else
-            put(std::integral_constant<int, CPOL_NT>());
-        return;
-    }
-    // the final product of a single-slice addmm: y = beta*C + alpha*p
-    __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(g.C ? g.C : g.Y) + (size_t)row0 * g.ldc + col0, 0, 0x7fffffff,
-        RAW_BUFFER_FLAGS);
-    void* ybase = g.out_bf16 ? (void*)(reinterpret_cast<uint16_t*>(g.Y) + (size_t)row0 * g.ldy + col0)
-                             : (void*)(g.Y + (size_t)row0 * g.ldy + col0);
-    const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc(ybase, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
-    u32x4 cv[ITER];
+            if (COHERENT || !g.epi) {
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    out + (size_t)prow0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+                auto put = [&](auto policy) {
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int v = tid + i * THREADS;
-        const int r = v / (BN / 4), c4 = v % (BN / 4);
-        const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
-        cv[i] = u32x4{0u, 0u, 0u, 0u};
-        if (g.C)
-            cv[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rc, in ? (int)((r * g.ldc + 4 * c4) * 4) : OOB, 0, 0);
-    }
+                    for (int i = 0; i < GROUP; ++i) {
+                        const int v = tid + (i0 + i) * T::THREADS;
+                        const int r = v / (BN / 4), c4 = v % (BN / 4);
+                        const bool in = (prow0 + r < M) && (col0 + 4 * c4 < N);
+                        const int off = in ? (r * ld + 4 * c4) * 4 : OOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0,
+                                                               decltype(policy)::value);
+                    }
+                };
+                if (COHERENT)
+                    put(std::integral_constant<int, CPOL_SC1>());
+                else if (g.out_z_stride)
+                    put(std::integral_constant<int, 0>());
+                else
+                    put(std::integral_constant<int, CPOL_NT>());
+                continue;
+            }
+            // the final product of a single-slice addmm: y = beta*C + alpha*p
+            __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(g.C ? g.C : g.Y) + (size_t)prow0 * g.ldc + col0, 0,
+                0x7fffffff, RAW_BUFFER_FLAGS);
+            void* ybase =
+                g.out_bf16 ? (void*)(reinterpret_cast<uint16_t*>(g.Y) + (size_t)prow0 * g.ldy + col0)
+                           : (void*)(g.Y + (size_t)prow0 * g.ldy + col0);
+            const __amdgpu_buffer_rsrc_t ry =
+                __builtin_amdgcn_make_buffer_rsrc(ybase, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+            u32x4 cv[GROUP];
 #pragma unroll
-    for (int i = 0; i < ITER; ++i) {
-        const int v = tid + i * THREADS;
-        const int r = v / (BN / 4), c4 = v % (BN / 4);
-        const bool in = (row0 + r < M) && (col0 + 4 * c4 < N);
-        float y[4];
+            for (int i = 0; i < GROUP; ++i) {
+                const int v = tid + (i0 + i) * T::THREADS;
+                const int r = v / (BN / 4), c4 = v % (BN / 4);
+                const bool in = (prow0 + r < M) && (col0 + 4 * c4 < N);
+                cv[i] = u32x4{0u, 0u, 0u, 0u};
+                if (g.C)
+                    cv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rc, in ? (int)((r * g.ldc + 4 * c4) * 4) : OOB, 0, 0);
+            }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            y[e] = epi_value(g, __uint_as_float(val[i][e]), __uint_as_float(cv[i][e]));
-        if (g.out_bf16) {
-            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 o = {f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16),
-                             f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16)};
-            __builtin_amdgcn_raw_buffer_store_b64(o, ry, in ? (int)((r * g.ldy + 4 * c4) * 2) : OOB,
-                                                  0, CPOL_NT);
-        } else {
-            const u32x4 o = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
-                             __float_as_uint(y[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(o, ry, in ? (int)((r * g.ldy + 4 * c4) * 4) : OOB,
-                                                   0, CPOL_NT);
+            for (int i = 0; i < GROUP; ++i) {
+                const int v = tid + (i0 + i) * T::THREADS;
+                const int r = v / (BN / 4), c4 = v % (BN / 4);
+                const bool in = (prow0 + r < M) && (col0 + 4 * c4 < N);
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = epi_value(g, __uint_as_float(val[i][e]), __uint_as_float(cv[i][e]));
+                if (g.out_bf16) {
+                    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 o = {f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16),
+                                     f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16)};
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        o, ry, in ? (int)((r * g.ldy + 4 * c4) * 2) : OOB, 0, CPOL_NT);
+                } else {
+                    const u32x4 o = {__float_as_uint(y[0]), __float_as_uint(y[1]),
+                                     __float_as_uint(y[2]), __float_as_uint(y[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        o, ry, in ? (int)((r * g.ldy + 4 * c4) * 4) : OOB, 0, CPOL_NT);
+                }
+            }
         }
     }
 }
 
-template <int STAGES, int CPS, int EPI, bool PARK, bool WT>
-__global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
+template <class T, int STAGES, int CPS, int EPI, bool PARK, bool WT>
+__global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
 {
+    constexpr int BM = T::BM, BN = T::BN, TM = T::TM, TN = T::TN, FM = T::FM, FN = T::FN;
+    constexpr int LOADS = T::LOADS, A_BYTES = T::A_BYTES, STAGE_BYTES = T::STAGE_BYTES;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int LOG = Log2<CPS>::value;
     constexpr int REG_LEVELS = PARK ? LOG - 1 : LOG;
-    constexpr int scratch_offset = STAGES * STAGE_BYTES + (PARK ? PARK_BYTES : 0);
+    constexpr int scratch_offset = STAGES * STAGE_BYTES + (PARK ? T::PARK_BYTES : 0);
     constexpr int NSTK = REG_LEVELS > 0 ? REG_LEVELS : 1;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
     const TileCoord tc = tile_coord(g, BM, BN);
     const int row0 = tc.row0, col0 = tc.col0;
     const int wrow0 = row0 + wm * TM, wcol0 = col0 + wn * TN;
-    // a wave whose whole 64 x 64 block lies past M or N skips the MFMAs
+    // a wave whose whole block lies past M or N skips the MFMAs
     const bool active = (wrow0 < g.M) && (wcol0 < g.N);
 
     // Buffer descriptors over the tile's rows of X and columns of W.  Reads
@@ -326,7 +370,8 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             const int n = s >> 3, cn = (s & 7) ^ (n & 7);  // B: row n, k-chunk cn
             offb[i] = (uint32_t)((n * g.ldw + 8 * cn) * 2);
         } else {
-            const int k = s >> 4, cb = (s & 15) ^ b_swz(k); // B: k-row k, n-chunk cb
+            const int k = s / T::B_ROW_CHUNKS;              // B: k-row k, n-chunk cb
+            const int cb = (s % T::B_ROW_CHUNKS) ^ b_swz(k);
             offb[i] = (uint32_t)((k * g.ldw + 8 * cb) * 2);
         }
     }
@@ -353,7 +398,7 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     };
     constexpr int LOADS_PER_ISSUE = 2 * LOADS;
 
-    // Fragment addresses inside a stage.  A: row r = wm*64 + fm*16 + lane%16,
+    // Fragment addresses inside a stage.  A: row r = wm*TM + fm*16 + lane%16,
     // k-chunk 4*ks + lane/16, swizzled by r%8 (= lane%8).  B: lane j of each
     // 16-lane group addresses k-row k0 + j/4 (k0 = 32ks + 8g + 4q) at
     // columns 4*(j%4) .. +3 of 16-column tile fn.
@@ -364,7 +409,7 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
         const int r = wm * TM + j;
         a_addr[ks] = (uint32_t)((r * 8 + ((4 * ks + gq) ^ (lane & 7))) * 16);
     }
-    // transposed W: row n = wn*64 + fn*16 + lane%16, k-chunk as for A
+    // transposed W: row n = wn*TN + fn*16 + lane%16, k-chunk as for A
     uint32_t bt_addr[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -378,7 +423,7 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
         const int k = 8 * gq + rr;                          // + 32ks + 4q added below
         const int n = wn * TN + fn * 16 + 4 * p;
         const int chunk = (n >> 3) ^ (2 * (rr + 4 * (gq & 1)));
-        b_addr[fn] = (uint32_t)(A_BYTES + (k * 16 + chunk) * 16 + ((n >> 2) & 1) * 8);
+        b_addr[fn] = (uint32_t)(A_BYTES + (k * T::B_ROW_CHUNKS + chunk) * 16 + ((n >> 2) & 1) * 8);
     }
 
     f32x4 acc[FM][FN];
@@ -409,9 +454,9 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
     bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
     auto frags = [&](bf16x8(&af)[FM], bf16x8(&bfr)[FN], const uint8_t* st, int ks) {
         if constexpr (WT)
-            load_frags_wt(af, bfr, st, a_addr[ks], bt_addr[ks]);
+            load_frags_wt<T>(af, bfr, st, a_addr[ks], bt_addr[ks]);
         else
-            load_frags(af, bfr, st, a_addr[ks], b_addr, ks);
+            load_frags<T>(af, bfr, st, a_addr[ks], b_addr, ks);
     };
     if (active)
         frags(fa0, fb0, smem, 0);
@@ -433,8 +478,8 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             __builtin_amdgcn_sched_barrier(0);
             if (active) {
                 frags(fa1, fb1, st, 1);
-                mma_step(acc, fa0, fb0);
-                interleave_reads_with_mfma<WT>();
+                mma_step<T>(acc, fa0, fb0);
+                interleave_reads_with_mfma<T, WT>();
             }
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkmcnt0();
@@ -451,8 +496,8 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
                 // the next block's reads are harmless after the last block
                 if (two_steps) {
                     frags(fa0, fb0, st_next, 0);
-                    mma_step(acc, fa1, fb1);
-                    interleave_reads_with_mfma<WT>();
+                    mma_step<T>(acc, fa1, fb1);
+                    interleave_reads_with_mfma<T, WT>();
                 } else {
                     frags(fa0, fb0, st_next, 0);
                 }
@@ -473,17 +518,14 @@ __global__ __launch_bounds__(THREADS) void lds_gemm_kernel(GemmArgs g)
             out = g.part + (size_t)tc.z * g.M * g.N;
             ld = g.N;
         }
-        store_tile_via_lds<EPI == EPI_COMBINE>(acc, g, out, ld, row0, col0, wm, wn, lane, tid,
-                                               smem);
+        store_tile_via_lds<T, STAGES, EPI == EPI_COMBINE>(acc, g, out, ld, row0, col0, wm, wn,
+                                                          lane, tid, smem);
         if constexpr (EPI == EPI_COMBINE) {
             int* s_last = reinterpret_cast<int*>(smem + scratch_offset + SCRATCH_BYTES);
-            arrive_and_combine<BM, BN, THREADS, CPS>(g, tc, tid, s_last);
+            arrive_and_combine<BM, BN, T::THREADS, CPS>(g, tc, tid, s_last);
         }
     }
 }
-
-static_assert(DETRED_LDS_STAGES * STAGE_BYTES >= BM * BN * 4 && 2 * STAGE_BYTES >= BM * BN * 4,
-              "the epilogue stages the fp32 tile in the stage buffers");
 
 template <int CPS>
 struct Stages {
@@ -493,19 +535,20 @@ struct Stages {
     static constexpr int value = park ? 2 : DETRED_LDS_STAGES;
 };
 
-template <int CPS, int EPI, bool WT>
+template <class T, int CPS, int EPI, bool WT>
 hipError_t launch(const GemmArgs& g, hipStream_t s)
 {
     constexpr int ST = Stages<CPS>::value;
     constexpr bool PK = Stages<CPS>::park;
-    auto fn = lds_gemm_kernel<ST, CPS, EPI, PK, WT>;
-    constexpr int bytes = ST * STAGE_BYTES + (PK ? PARK_BYTES : 0) + SCRATCH_BYTES + 16;
+    auto fn = lds_gemm_kernel<T, ST, CPS, EPI, PK, WT>;
+    constexpr int bytes = ST * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) + SCRATCH_BYTES + 16;
+    static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (attr != hipSuccess)
         return attr;
     const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(THREADS), bytes, s, g);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(T::THREADS), bytes, s, g);
     return hipGetLastError();
 }
 
@@ -513,52 +556,61 @@ template <int EPI, bool WT>
 hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (cps) {
-    case 1: return launch<1, EPI, WT>(g, s);
-    case 2: return launch<2, EPI, WT>(g, s);
-    case 4: return launch<4, EPI, WT>(g, s);
+    case 1: return launch<Tile128, 1, EPI, WT>(g, s);
+    case 2: return launch<Tile128, 2, EPI, WT>(g, s);
+    case 4: return launch<Tile128, 4, EPI, WT>(g, s);
     case 8:
         if constexpr (EPI == EPI_COMBINE)
             return hipErrorInvalidValue;
         else
-            return launch<8, EPI, WT>(g, s);
+            return launch<Tile128, 8, EPI, WT>(g, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int EPI>
-hipError_t launch_layout(const GemmArgs& g, int cps, hipStream_t s)
+hipError_t launch_layout(int tile, const GemmArgs& g, int cps, hipStream_t s)
 {
+    if (tile == TILE_L256) {
+        // one-chunk slices writing their roots (shards) only
+        if (cps != 1 || EPI != EPI_STORE)
+            return hipErrorInvalidValue;
+        if constexpr (EPI == EPI_STORE)
+            return g.wt ? launch<Tile256, 1, EPI, true>(g, s) : launch<Tile256, 1, EPI, false>(g, s);
+    }
     return g.wt ? launch_cps<EPI, true>(g, cps, s) : launch_cps<EPI, false>(g, cps, s);
 }
 
 }  // namespace lds
 
-bool lds_engine_supports(const GemmArgs& g, int cps)
+bool lds_engine_supports(int tile, const GemmArgs& g, int cps)
 {
-    (void)cps;
     // every MFMA step inside K, and byte offsets of the tile's X rows, W
     // columns and output rows within the 31-bit record range of a buffer
-    // descriptor
-    if (g.Kc % 32 != 0)
+    // descriptor; the 256x256 tile for one-chunk slices only
+    if (g.Kc % 32 != 0 || (tile != TILE_L128 && tile != TILE_L256))
         return false;
-    const size_t xbytes = ((size_t)(lds::BM - 1) * g.ldx + g.K) * 2;
-    const size_t wbytes = g.wt ? ((size_t)(lds::BN - 1) * g.ldw + g.K) * 2
-                               : ((size_t)g.K * g.ldw) * 2;
+    if (tile == TILE_L256 && cps != 1)
+        return false;
+    const size_t BM = tile == TILE_L256 ? lds::Tile256::BM : lds::Tile128::BM;
+    const size_t BN = tile == TILE_L256 ? lds::Tile256::BN : lds::Tile128::BN;
+    const size_t xbytes = ((BM - 1) * g.ldx + g.K) * 2;
+    const size_t wbytes = g.wt ? ((BN - 1) * g.ldw + g.K) * 2 : ((size_t)g.K * g.ldw) * 2;
     // output rows of the tile (Y at ldy, partial planes at N, C at ldc)
     // likewise
     size_t ld = (size_t)(g.ldy > g.N ? g.ldy : g.N);
     if (g.epi && g.C && (size_t)g.ldc > ld)
         ld = (size_t)g.ldc;
-    const size_t ybytes = ((lds::BM - 1) * ld + lds::BN) * 4;
+    const size_t ybytes = ((BM - 1) * ld + BN) * 4;
     return xbytes < 0x7fffffffu && wbytes < 0x7fffffffu && ybytes < 0x7fffffffu;
 }
 
-hipError_t launch_lds_gemm(int epi, const GemmArgs& g, int cps, hipStream_t s)
+hipError_t launch_lds_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (epi) {
-    case EPI_STORE: return lds::launch_layout<EPI_STORE>(g, cps, s);
-    case EPI_COMBINE: return lds::launch_layout<EPI_COMBINE>(g, cps, s);
-    case EPI_ATOMIC: return lds::launch_layout<EPI_ATOMIC>(g, cps, s);
+    case EPI_STORE: return lds::launch_layout<EPI_STORE>(tile, g, cps, s);
+    case EPI_COMBINE: return lds::launch_layout<EPI_COMBINE>(tile, g, cps, s);
+    case EPI_ATOMIC: return lds::launch_layout<EPI_ATOMIC>(tile, g, cps, s);
     }
     return hipErrorInvalidValue;
 }

@@ -85,8 +85,11 @@ def test_position_invariance(dev):
         assert_bitwise(yp, ref[perm], "permuted rows, shape %s" % ((M, N, K),))
 
 
+# the last two shapes put the 8-shard roots (chunks of 1024) on the
+# 256x256 tile, with ragged M and N; the last also each shard at its share
+# shape
 @pytest.mark.parametrize("M,N,K", [(16, 16, 512), (256, 64, 4096), (128, 14336, 4096),
-                                   (512, 8192, 8192)])
+                                   (512, 8192, 8192), (520, 3080, 8192), (4100, 4104, 8192)])
 def test_split_and_tp_invariance(M, N, K, dev):
     """det S in {1,2,4,8} and tree_tp T in {1,2,4,8} give one bit pattern;
     so does every shard run at its own share shape plus the tree combine."""
