@@ -1,7 +1,7 @@
 // LDS-DMA slice GEMM engine for gfx950: the wide-output workgroup tiles,
-// 128x128 (four waves of 64x64, any chunk count) and 256x256 (eight waves
-// of 128x64, one-chunk slices only: its accumulators leave no registers for
-// a subtree).  Same reduction order, output values and last-arriver combine
+// 128x128 (eight waves of 64x32, any chunk count; four of 64x64 for
+// one-chunk root stores) and 256x256 (eight waves of 128x64, one-chunk
+// slices only: its accumulators leave no registers for a subtree).  Same reduction order, output values and last-arriver combine
 // as the register-staged engine (gemm_common.h); the data movement differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
@@ -61,7 +61,15 @@ struct LdsTile {
     static_assert(LOADS * THREADS * 16 == A_BYTES && LOADS * THREADS * 16 == B_BYTES,
                   "A and B take the same whole number of loads per lane");
 };
-using Tile128 = LdsTile<128, 128, 2, 2>;
+// Eight waves (two per SIMD) rather than four of 64x64: the second wave of
+// each SIMD issues while the first waits on LDS or on its loads (dense
+// 256x14336x4096 54.8 -> 51.7 us, 4096 rows 672 -> 628 us, one row at
+// 8 slices 35.3 -> 31.0 us on MI355X; same bits).
+using Tile128 = LdsTile<128, 128, 2, 4>;
+// Four waves of 64x64 for one-chunk slices that store their roots (shards
+// not on the 256x256 tile): there the eight-wave form is slower (8 shards
+// of 512x8192x8192: 104 vs 112 us; 4096x4096x4096: 238 vs 245 us).
+using Tile128x4 = LdsTile<128, 128, 2, 2>;
 using Tile256 = LdsTile<256, 256, 2, 4>;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -556,7 +564,11 @@ template <int EPI, bool WT>
 hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (cps) {
-    case 1: return launch<Tile128, 1, EPI, WT>(g, s);
+    case 1:
+        if constexpr (EPI == EPI_STORE)
+            return launch<Tile128x4, 1, EPI, WT>(g, s);
+        else
+            return launch<Tile128, 1, EPI, WT>(g, s);
     case 2: return launch<Tile128, 2, EPI, WT>(g, s);
     case 4: return launch<Tile128, 4, EPI, WT>(g, s);
     case 8:
