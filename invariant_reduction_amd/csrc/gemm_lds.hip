@@ -535,21 +535,29 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     }
 }
 
-template <int CPS>
+// With 8 chunks per slice the top subtree level is parked in LDS, beside
+// three stages: 96 + 64 KiB, the whole LDS of the CU.  The third stage keeps
+// two weight blocks in flight per workgroup, which is what a product whose
+// weights come from HBM needs (256x14336x4096 with the weights not cached:
+// 67.5 -> 53.4 us, 1024 rows 234 -> 185 us on MI355X), at a few percent on
+// repeated calls whose weights stay in the MALL.
+template <class T, int CPS>
 struct Stages {
-    // with 8 chunks per slice the top subtree level is parked in LDS and
-    // fewer stages fit
     static constexpr bool park = (CPS == 8);
-    static constexpr int value = park ? 2 : DETRED_LDS_STAGES;
+    static constexpr int fit = (DETRED_LDS_STAGES * T::STAGE_BYTES + 16 <= 160 * 1024)
+                                   ? DETRED_LDS_STAGES : 2;
+    static constexpr int value = park ? 3 : fit;
 };
 
 template <class T, int CPS, int EPI, bool WT>
 hipError_t launch(const GemmArgs& g, hipStream_t s)
 {
-    constexpr int ST = Stages<CPS>::value;
-    constexpr bool PK = Stages<CPS>::park;
+    constexpr int ST = Stages<T, CPS>::value;
+    constexpr bool PK = Stages<T, CPS>::park;
     auto fn = lds_gemm_kernel<T, ST, CPS, EPI, PK, WT>;
-    constexpr int bytes = ST * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) + SCRATCH_BYTES + 16;
+    // + the last-arriver flag of a combine (never with 8 chunks per slice)
+    constexpr int bytes = ST * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) + SCRATCH_BYTES +
+                          (EPI == EPI_COMBINE ? 16 : 0);
     static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
