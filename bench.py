@@ -13,11 +13,13 @@ vocabulary 151936), batch 256:
                                      subtree roots (what each rank computes)
   tp_combine   tree_combine_f32      the top 3 tree levels over the 8 roots
                                      (what the cross-rank reduction computes)
-  log_softmax  inv_log_softmax       logits[256,151936] fp32
-  mean         inv_mean              logits[256,151936] fp32
+  log_softmax_mean inv_log_softmax_mean logits[256,151936] fp32: log_softmax
+                                     and the row mean in one pass over the
+                                     logits (the bits of inv_log_softmax and
+                                     inv_mean, which are checked against it)
 Every operation runs in libdetred's HIP kernels.  The step's three
-independent chains (dense -> log_softmax; the tree-TP pair; rmsnorm, the
-LoRA shrink/control/cast/expand and mean) run on three streams of default
+independent chains (dense -> log_softmax_mean; the tree-TP pair; rmsnorm,
+the LoRA shrink/control/cast/expand) run on three streams of default
 priority, forked from and joined to the main stream with events; the same
 ops issued serially on one stream are timed too (ms_per_step_serial).
 `value` is the deterministic GEMM work of a step (shrink, expand, dense,
@@ -57,7 +59,7 @@ TP_M, TP_K, TP_N, TP_T = 512, 8192, 8192, 8
 
 WORKLOAD = ("hot_path_8b_b256: rmsnorm[256,4096]; lora shrink X[256,4096]A[4096,64] det split-K=8 "
             "(+atomic control); bf16 cast; expand [256,64]B[64,4096]; dense X[256,4096]W[4096,14336]; "
-            "tree-TP X[512,8192]W[8192,8192] T=8; log_softmax+mean logits[256,151936]")
+            "tree-TP X[512,8192]W[8192,8192] T=8; log_softmax+mean logits[256,151936] (one pass)")
 
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -101,8 +103,8 @@ class Workload:
         split partials and shard buffers are not credited (tp_shards: X, W
         and one [M,N] result).  Each launch re-issues a C call whose arguments were
         marshalled once, on streams[lane].  Lanes are independent chains:
-        0 dense -> log_softmax; 1 the tree-TP pair; 2 rmsnorm, the LoRA
-        shrink/control/cast/expand and mean."""
+        0 dense -> log_softmax_mean; 1 the tree-TP pair; 2 rmsnorm, the
+        LoRA shrink/control/cast/expand."""
         gb = 2  # bytes per bf16
 
         def P(lane, fn, *args):
@@ -124,10 +126,9 @@ class Workload:
              2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_M * TP_N * 4, 1),
             ("tp_combine", P(1, detred.tree_combine_f32, self.p_tp, self.y_tp),
              0, TP_T * TP_M * TP_N * 4 + TP_M * TP_N * 4, 1),
-            ("log_softmax", P(0, detred.inv_log_softmax, self.lg, self.y_lsm),
-             0, 2 * B * V * 4, 0),
-            ("mean", P(2, detred.inv_mean, self.lg, self.y_mean),
-             0, B * V * 4 + B * 4, 2),
+            ("log_softmax_mean", P(0, detred.inv_log_softmax_mean, self.lg, self.y_lsm,
+                                   self.y_mean),
+             0, 2 * B * V * 4 + B * 4, 0),
         ]
 
 
@@ -257,8 +258,8 @@ def invariance(wl, dev):
 
     def cmp(a, b):
         nonlocal same, total
-        a = a.view(torch.int32)
-        b = b.view(torch.int32)
+        a = a.view(torch.int32).reshape(a.shape[0], -1)
+        b = b.view(torch.int32).reshape(b.shape[0], -1)
         eq = torch.all(a == b, dim=1)
         same += int(eq.sum())
         total += eq.numel()
@@ -297,6 +298,9 @@ def invariance(wl, dev):
         y = torch.empty((Bp, V), dtype=f32, device=dev)
         detred.inv_log_softmax(wl.lg[:Bp], y)
         cmp(y, wl.y_lsm[:Bp])
+        y = torch.empty((Bp,), dtype=f32, device=dev)
+        detred.inv_mean(wl.lg[:Bp], y)
+        cmp(y, wl.y_mean[:Bp])
     torch.cuda.synchronize()
     return same, total
 
@@ -647,7 +651,7 @@ def main():
 
     # replays: every deterministic output is reproduced bit for bit; the
     # atomic control is counted
-    ref = {k: getattr(wl, k).clone() for k in ("y_shr", "y_dns", "y_tp", "y_lsm", "y_rms")}
+    ref = {k: getattr(wl, k).clone() for k in ("y_shr", "y_dns", "y_tp", "y_lsm", "y_mean", "y_rms")}
     atom0 = None
     det_same = atom_diff = 0
     for r in range(20):

@@ -331,6 +331,18 @@ int inv_log_softmax(const float *x, float *y, int rows, int cols,
 int inv_mean(const float *x, float *y, int rows, int cols, detred_stream s);
 
 /*
+ * inv_log_softmax and inv_mean of the same rows in one pass over x: y as
+ * inv_log_softmax gives it and mu[r] as inv_mean gives it, bit for bit (the
+ * mean takes the order and tree inv_mean uses), with x read once instead of
+ * twice: two of the operations the "Batch Invariant Ops" project makes
+ * batch invariant (Highlighted Details) in one kernel.  mu fp32 [rows],
+ * 4-byte aligned; other arguments and errors as inv_log_softmax (x and y may
+ * be the same buffer).
+ */
+int inv_log_softmax_mean(const float *x, float *y, float *mu, int rows, int cols,
+                         detred_stream s);
+
+/*
  * Workspace of inv_decode_attention: the per-chunk results of B*Hq query
  * rows over ceil(max_len/256) chunks (D + 2 floats each), 256-byte aligned
  * sections.  0 for invalid arguments.

@@ -610,6 +610,19 @@ int inv_log_softmax(const float* x, float* y, int rows, int cols, detred_stream 
     return hip_status(launch_log_softmax(x, y, rows, cols, (hipStream_t)s));
 }
 
+int inv_log_softmax_mean(const float* x, float* y, float* mu, int rows, int cols, detred_stream s)
+{
+    if (rows < 0 || cols < 0)
+        return DETRED_EINVAL;
+    if (rows == 0)
+        return DETRED_OK;
+    if (!x || !y || !mu || !aligned16(x) || !aligned16(y) || ((uintptr_t)mu & 3u))
+        return DETRED_EINVAL;
+    if (cols == 0 || cols % 4 != 0)
+        return DETRED_EUNSUPPORTED;
+    return hip_status(launch_log_softmax_mean(x, y, mu, rows, cols, (hipStream_t)s));
+}
+
 int inv_mean(const float* x, float* y, int rows, int cols, detred_stream s)
 {
     if (rows < 0 || cols < 0)

@@ -79,6 +79,8 @@ int attention_chunk();
 hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s);
+hipError_t launch_log_softmax_mean(const float* x, float* y, float* mu, int rows, int cols,
+                                   hipStream_t s);
 hipError_t launch_mean(const float* x, float* y, int rows, int cols, hipStream_t s);
 
 }  // namespace detred

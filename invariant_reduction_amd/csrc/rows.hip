@@ -117,7 +117,6 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
 // 40 + 18 vectors, 464 KiB of a row, 78% of a 151936-wide row); only the
 // rest is read from memory a second time.  The visit order is that of
 // every row kernel here (thread t: vectors t, t+NT, t+2NT, ...).
-constexpr int ROW_THREADS = 1024;  // mean
 constexpr int UNROLL = 4;          // 16-byte loads in flight per thread
 constexpr int LSM_THREADS = 512;
 constexpr int LSM_REG = 40;
@@ -149,11 +148,15 @@ __device__ __forceinline__ void store_shifted(float4* p, const float4 q, float m
     __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
 }
 
+// MEAN: the row mean is taken in the same pass (mu[row]), with the order,
+// thread count and tree of mean_kernel, so its bits are inv_mean's.
+template <bool MEAN>
 __global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x, float* y,
-                                                                  int cols)
+                                                                  float* mu, int cols)
 {
     extern __shared__ float4 cache[];  // LSM_LDS vectors per thread
     __shared__ float red_m[LSM_THREADS / 64], red_s[LSM_THREADS / 64];
+    __shared__ float red_sum[LSM_THREADS / 64];
     constexpr int NT = LSM_THREADS;
     const int tid = threadIdx.x;
     const size_t row = blockIdx.x;
@@ -165,8 +168,14 @@ __global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x
     // exp of an element: the hardware base-2 exponential of (x - m)*log2(e)
     // (__expf), relative error about 2e-6 for |x - m| <= 30, a fixed
     // function like any other; the rescales of the running sum use expf
-    float m = -INFINITY, s = 0.0f;
+    float m = -INFINITY, s = 0.0f, sum = 0.0f;
     auto visit = [&](const float4 q) {
+        if (MEAN) {
+            sum = sum + q.x;
+            sum = sum + q.y;
+            sum = sum + q.z;
+            sum = sum + q.w;
+        }
         const float mx = fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w));
         if (mx > m) {
             s = s * expf(m - mx);
@@ -244,6 +253,11 @@ __global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x
     m = __shfl(m, 0, 64);
     s = __shfl(s, 0, 64);
     const float ls = logf(s);
+    if constexpr (MEAN) {
+        const float total = block_sum<LSM_THREADS / 64>(sum, red_sum);
+        if (tid == 0)
+            mu[row] = total / (float)cols;
+    }
 
     // second pass: cached vectors from registers and LDS, the rest re-read
 #pragma unroll
@@ -273,6 +287,12 @@ __global__ __launch_bounds__(LSM_THREADS) void log_softmax_kernel(const float* x
 }
 
 // --------------------------------------------------------------------- mean
+// The thread count, per-thread visit order and tree of log_softmax's first
+// pass, so the mean fused into log_softmax has the same bits; MEAN_UNROLL
+// loads in flight per thread.
+constexpr int ROW_THREADS = LSM_THREADS;
+constexpr int MEAN_UNROLL = 8;
+
 __global__ __launch_bounds__(ROW_THREADS) void mean_kernel(const float* __restrict__ x,
                                                            float* __restrict__ y, int cols)
 {
@@ -288,13 +308,13 @@ __global__ __launch_bounds__(ROW_THREADS) void mean_kernel(const float* __restri
         s = s + q.w;
     };
     int v = threadIdx.x;
-    for (; v + (UNROLL - 1) * ROW_THREADS < nv; v += UNROLL * ROW_THREADS) {
-        float4 q[UNROLL];
+    for (; v + (MEAN_UNROLL - 1) * ROW_THREADS < nv; v += MEAN_UNROLL * ROW_THREADS) {
+        float4 q[MEAN_UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < MEAN_UNROLL; ++u)
             q[u] = xr[v + u * ROW_THREADS];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < MEAN_UNROLL; ++u)
             visit(q[u]);
     }
     for (; v < nv; v += ROW_THREADS)
@@ -320,16 +340,29 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_
     return hipGetLastError();
 }
 
-hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s)
+template <bool MEAN>
+static hipError_t launch_lsm(const float* x, float* y, float* mu, int rows, int cols,
+                             hipStream_t s)
 {
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(log_softmax_kernel),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(log_softmax_kernel<MEAN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LSM_LDS_BYTES);
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL(log_softmax_kernel, dim3(rows), dim3(LSM_THREADS), LSM_LDS_BYTES, s, x, y,
-                       cols);
+    hipLaunchKernelGGL(log_softmax_kernel<MEAN>, dim3(rows), dim3(LSM_THREADS), LSM_LDS_BYTES, s,
+                       x, y, mu, cols);
     return hipGetLastError();
+}
+
+hipError_t launch_log_softmax(const float* x, float* y, int rows, int cols, hipStream_t s)
+{
+    return launch_lsm<false>(x, y, nullptr, rows, cols, s);
+}
+
+hipError_t launch_log_softmax_mean(const float* x, float* y, float* mu, int rows, int cols,
+                                   hipStream_t s)
+{
+    return launch_lsm<true>(x, y, mu, rows, cols, s);
 }
 
 hipError_t launch_mean(const float* x, float* y, int rows, int cols, hipStream_t s)

@@ -53,6 +53,7 @@ SIGNATURES = {
     "inv_rmsnorm_bf16": ([_P, _P, _P, _I, _I, _F, _P], _I),
     "inv_log_softmax": ([_P, _P, _I, _I, _P], _I),
     "inv_mean": ([_P, _P, _I, _I, _P], _I),
+    "inv_log_softmax_mean": ([_P, _P, _P, _I, _I, _P], _I),
     "inv_decode_attention_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "inv_decode_attention": ([_P, _P, _P, ctypes.c_long, ctypes.c_long, ctypes.c_long, _P, _P,
                               _I, _I, _I, _I, _I, _F, _P, _Z, _P], _I),
@@ -415,6 +416,20 @@ def inv_mean(x, y, stream=None):
     if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.numel() != rows:
         raise TypeError("y must be a contiguous fp32 GPU vector with one element per row")
     return "inv_mean", (px, ctypes.c_void_p(y.data_ptr()), rows, cols, _stream(stream))
+
+
+@_entry
+def inv_log_softmax_mean(x, y, mu, stream=None):
+    """y = log_softmax(x) and mu = mean(x) over the last dim (fp32), one pass
+    over x; the bits of inv_log_softmax and inv_mean."""
+    px, rows, cols = _rows(x, (torch.float32,), "x")
+    py, rows2, cols2 = _rows(y, (torch.float32,), "y")
+    if (rows2, cols2) != (rows, cols):
+        raise ValueError("x and y must have the same shape")
+    if mu.dtype != torch.float32 or not mu.is_cuda or not mu.is_contiguous() or mu.numel() != rows:
+        raise TypeError("mu must be a contiguous fp32 GPU vector with one element per row")
+    return "inv_log_softmax_mean", (px, py, ctypes.c_void_p(mu.data_ptr()), rows, cols,
+                                    _stream(stream))
 
 
 def inv_decode_attention_workspace_bytes(B, Hq, D, max_len):

@@ -168,6 +168,11 @@ def test_other_entry_points_reject():
     assert L.inv_log_softmax(MIS, A16b, 4, 8, None) == detred.EINVAL
     assert L.inv_mean(A16, A16b, 4, 0, None) == detred.EUNSUPPORTED
     assert L.inv_mean(None, A16b, 4, 8, None) == detred.EINVAL
+    assert L.inv_log_softmax_mean(A16, A16b, A16c, 4, 6, None) == detred.EUNSUPPORTED
+    assert L.inv_log_softmax_mean(A16, A16b, None, 4, 8, None) == detred.EINVAL
+    assert L.inv_log_softmax_mean(A16, MIS, A16c, 4, 8, None) == detred.EINVAL
+    assert L.inv_log_softmax_mean(A16, A16b, A16c + 2, 4, 8, None) == detred.EINVAL
+    assert L.inv_log_softmax_mean(None, None, None, 0, 8, None) == detred.OK
     assert L.detred_workspace_init(None, 16, None) == detred.EINVAL
 
 

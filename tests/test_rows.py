@@ -128,3 +128,27 @@ def test_logit_ops_batch_invariance(dev):
         torch.cuda.synchronize()
         assert_bitwise(yl[0], ref_l[j], "log_softmax row %d alone" % j)
         assert_bitwise(ym[0], ref_m[j], "mean row %d alone" % j)
+
+
+@pytest.mark.parametrize("B,V", [(1, 151936), (256, 151936), (3, 4), (5, 1000), (9, 65540),
+                                 (2, 4100)])
+def test_log_softmax_mean_fused_equals_separate(B, V, dev):
+    """One pass over x gives inv_log_softmax's and inv_mean's bits (the mean
+    shares their thread count, visit order and tree); in place too."""
+    x = inputs.logits_inputs(B, V, seed=11 * B + V)
+    xd = dev_f32(x, dev)
+    yl = torch.empty_like(xd)
+    ym = torch.empty(B, dtype=torch.float32, device=dev)
+    detred.inv_log_softmax(xd, yl)
+    detred.inv_mean(xd, ym)
+    fl = torch.full_like(xd, float("nan"))
+    fm = torch.full((B,), float("nan"), dtype=torch.float32, device=dev)
+    detred.inv_log_softmax_mean(xd, fl, fm)
+    xi = xd.clone()
+    mi = torch.empty(B, dtype=torch.float32, device=dev)
+    detred.inv_log_softmax_mean(xi, xi, mi)
+    torch.cuda.synchronize()
+    assert_bitwise(fl, yl, "fused log_softmax")
+    assert_bitwise(fm, ym, "fused mean")
+    assert_bitwise(xi, yl, "fused in place")
+    assert_bitwise(mi, ym, "fused mean, in place")
