@@ -106,8 +106,9 @@ int detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
  * only decides how many workgroups share the chunk tree; the bits of the
  * result never depend on it (nor on M).  Outputs of at most 64 columns use
  * one slice per chunk (S = P).  Wider ones use S = 1 when their tiles
- * already cover at least 192 CUs, else the smallest S (<= P) with
- * tiles*S >= 256.  Returns 0 for invalid arguments.
+ * already cover at least 192 CUs, else S = 4, or 8 (<= P) while
+ * tiles*S < 256 (two slices are never chosen: they are slower than four).
+ * Returns 0 for invalid arguments.
  */
 int detred_auto_split(int M, int N, int K);
 

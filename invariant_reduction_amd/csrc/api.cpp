@@ -154,9 +154,12 @@ void widen_for_roots(Policy& p, GemmArgs& g, int cps)
 // share the chunk tree, never the bits.  Narrow outputs keep the policy's
 // split (one slice per chunk).  A wide product splits while its output tiles
 // leave CUs idle: S = 1 once the tiles cover 192 CUs (there the extra
-// partial traffic costs more than the idle CUs), else the smallest S with
-// tiles*S >= 256.  Chosen from timings of 1..1024-row products with
-// N in {1024, 4096, 14336} and K in {4096, 8192} on MI355X.
+// partial traffic costs more than the idle CUs), else S = 4, or 8 while
+// tiles*S < 256.  Two slices of four chunks are never the fastest: with the
+// weights coming from HBM, 512x4096x14336 takes 113 / 89 us at S = 2 / 4,
+// 512x4096x4096 44 / 42 us, 2048x1024x8192 72 / 61 us on MI355X.  Chosen
+// from timings of 1..2048-row products with N in {1024, 4096, 8192, 14336}
+// and K in {4096, 8192, 14336}.
 int auto_split(const Policy& p, int M, int N)
 {
     if (p.tile != TILE_L128)
@@ -164,7 +167,7 @@ int auto_split(const Policy& p, int M, int N)
     const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     if (tiles >= 192)
         return 1;
-    int S = 1;
+    int S = p.P < 4 ? p.P : 4;
     while (S < p.P && tiles * S < 256)
         S *= 2;
     return S;

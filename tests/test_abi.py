@@ -60,7 +60,7 @@ def test_auto_split():
     assert detred.auto_split(256, 14336, 4096) == 1      # 224 tiles
     assert detred.auto_split(1, 14336, 4096) == 4        # 112 tiles
     assert detred.auto_split(256, 4096, 4096) == 4       # 64 tiles
-    assert detred.auto_split(512, 4096, 4096) == 2       # 128 tiles
+    assert detred.auto_split(512, 4096, 4096) == 4       # 128 tiles: two slices are skipped
     assert detred.auto_split(1, 1024, 4096) == 8         # 8 tiles, capped at P
     assert detred.auto_split(1024, 4096, 4096) == 1      # 256 tiles
     assert detred.auto_split(1, 4096, 64) == 1           # one chunk
