@@ -485,6 +485,10 @@ def config_sweep(dev, stream):
         del ys
         ym = torch.empty((Bn,), dtype=torch.float32, device=dev)
         rec("mean_b%d" % Bn, detred.prepare(detred.inv_mean, lg, ym), 0, Bn * V * 4 + Bn * 4)
+        ys = torch.empty_like(lg)
+        rec("log_softmax_mean_b%d" % Bn,
+            detred.prepare(detred.inv_log_softmax_mean, lg, ys, ym), 0, 2 * Bn * V * 4 + Bn * 4)
+        del ys
         del lg
     return out
 
