@@ -150,6 +150,24 @@ void widen_for_roots(Policy& p, GemmArgs& g, int cps)
     g = w;
 }
 
+// Products of at most 32 rows on the 32x128 tile: the same tile count as
+// 128x128 (one tile row either way, so the split, the workspace and the
+// arrival counters are unchanged), but a quarter of the A block, so four
+// stages of weights are in flight instead of two.  The tile never changes
+// the bits.
+void narrow_for_decode(Policy& p, GemmArgs& g, int cps)
+{
+    if (p.tile != TILE_L128 || g.M > 32)
+        return;
+    GemmArgs w = g;
+    w.tiles_m = 1;
+    if (!lds_engine_supports(TILE_D32, w, cps))
+        return;
+    p.tile = TILE_D32;
+    tile_shape(p.tile, &p.bm, &p.bn);
+    g = w;
+}
+
 // The split for split_k = 0.  The split only decides how many workgroups
 // share the chunk tree, never the bits.  Narrow outputs keep the policy's
 // split (one slice per chunk).  A wide product splits while its output tiles
@@ -250,13 +268,16 @@ namespace {
 
 // The deterministic product (and its epilogue, when g.epi) with S slices:
 // one launch; with S > 1 the partials and counters live in ws.
-int run_det(const Policy& p, GemmArgs g, int S, void* ws, size_t ws_bytes, hipStream_t hs)
+int run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_bytes, hipStream_t hs)
 {
+    Policy p = p0;
     if (g.K == 0)
         return hip_status(g.epi ? launch_epilogue_only(g, hs)
                                 : launch_fill_zero(g.Y, g.ldy, g.M, g.N, hs));
-    if (S == 1)
+    if (S == 1) {
+        narrow_for_decode(p, g, p.P);
         return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
+    }
     // the last-arriver combine addresses a tile's rows with 32-bit offsets
     if ((size_t)(p.bm - 1) * g.N + p.bn >= ((size_t)1 << 29))
         return DETRED_EUNSUPPORTED;
@@ -265,6 +286,7 @@ int run_det(const Policy& p, GemmArgs g, int S, void* ws, size_t ws_bytes, hipSt
         return DETRED_EWORKSPACE;
     g.part = (float*)ws;
     g.counters = (unsigned*)((char*)ws + partial_bytes(g.M, g.N, S));
+    narrow_for_decode(p, g, p.P / S);
     return hip_status(launch_slice_gemm(p.tile, EPI_COMBINE, g, p.P / S, hs));
 }
 
@@ -462,7 +484,9 @@ int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, f
     if (e != hipSuccess || K == 0)
         return hip_status(e);
     GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
-    return hip_status(launch_slice_gemm(p.tile, EPI_ATOMIC, g, p.P / S, hs));
+    Policy pa = p;
+    narrow_for_decode(pa, g, p.P / S);
+    return hip_status(launch_slice_gemm(pa.tile, EPI_ATOMIC, g, p.P / S, hs));
 }
 
 int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
@@ -479,8 +503,10 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     if (K == 0)
         return hip_status(launch_fill_zero(Y, ldy, M, N, hs));
     GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, T);
-    if (T == 1)
+    if (T == 1) {
+        narrow_for_decode(p, g, p.P);
         return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
+    }
     if (!ws || !aligned256(ws) || ws_bytes < partial_bytes(M, N, T))
         return DETRED_EWORKSPACE;
     // phase 1: every shard writes its subtree root to its own buffer
@@ -488,6 +514,7 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     g.ldy = N;
     g.out_z_stride = (long)M * N;
     widen_for_roots(p, g, p.P / T);
+    narrow_for_decode(p, g, p.P / T);
     hipError_t e = launch_slice_gemm(p.tile, EPI_STORE, g, p.P / T, hs);
     if (e != hipSuccess)
         return DETRED_EHIP;
@@ -521,6 +548,7 @@ int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, 
     GemmArgs g = make_args(p, X, ldx, W, ldw, P, N, M, N, K, tp_shards);
     g.out_z_stride = (long)M * N;
     widen_for_roots(p, g, p.P / tp_shards);
+    narrow_for_decode(p, g, p.P / tp_shards);
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
 }
 
@@ -545,6 +573,7 @@ int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
     // the shard's own K range is chunks [0, P/T) of width K/P
     GemmArgs g = make_args(p, Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, 1);
     widen_for_roots(p, g, p.P / tp_shards);
+    narrow_for_decode(p, g, p.P / tp_shards);
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
 }
 

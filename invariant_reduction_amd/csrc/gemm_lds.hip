@@ -1,7 +1,8 @@
 // LDS-DMA slice GEMM engine for gfx950: the wide-output workgroup tiles,
 // 128x128 (eight waves of 64x32, any chunk count; four of 64x64 for
-// one-chunk root stores) and 256x256 (eight waves of 128x64, one-chunk
-// slices only: its accumulators leave no registers for a subtree).  Same reduction order, output values and last-arriver combine
+// one-chunk root stores), 256x256 (eight waves of 128x64, one-chunk slices
+// only: its accumulators leave no registers for a subtree) and 32x128 for
+// products of at most 32 rows (four waves of 32x32).  Same reduction order, output values and last-arriver combine
 // as the register-staged engine (gemm_common.h); the data movement differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
@@ -55,11 +56,14 @@ struct LdsTile {
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LOADS = A_BYTES / (THREADS * 16);  // 16-byte loads per lane per operand
+    // 16-byte loads per lane of a stage's A and B blocks
+    static constexpr int LOADS_A = A_BYTES / (THREADS * 16);
+    static constexpr int LOADS_B = B_BYTES / (THREADS * 16);
     static constexpr int B_ROW_CHUNKS = BN / 8;              // 16-byte chunks per k-row of B
     static constexpr int PARK_BYTES = WAVES * FM * FN * 64 * 16;  // one subtree level
-    static_assert(LOADS * THREADS * 16 == A_BYTES && LOADS * THREADS * 16 == B_BYTES,
-                  "A and B take the same whole number of loads per lane");
+    static_assert(LOADS_A >= 1 && LOADS_A * THREADS * 16 == A_BYTES &&
+                      LOADS_B * THREADS * 16 == B_BYTES,
+                  "A and B blocks take whole numbers of loads per lane");
 };
 // Eight waves (two per SIMD) rather than four of 64x64: the second wave of
 // each SIMD issues while the first waits on LDS or on its loads (dense
@@ -71,6 +75,9 @@ using Tile128 = LdsTile<128, 128, 2, 4>;
 // of 512x8192x8192: 104 vs 112 us; 4096x4096x4096: 238 vs 245 us).
 using Tile128x4 = LdsTile<128, 128, 2, 2>;
 using Tile256 = LdsTile<256, 256, 2, 4>;
+// Products of at most 32 rows (decode): 32x128, four waves of 32x32.  The
+// A block shrinks to 4 KiB, so the LDS holds more weight blocks in flight.
+using TileD32 = LdsTile<32, 128, 1, 4>;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -128,6 +135,20 @@ __device__ __forceinline__ void wait_lgkmcnt0()
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// MFMA I of N followed by its share of the READS reads, PER at most.
+template <int I, int N, int READS, int PER>
+__device__ __forceinline__ void spread_reads()
+{
+    if constexpr (I < N) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        constexpr int left = READS - I * PER;
+        constexpr int here = left < PER ? (left > 0 ? left : 0) : PER;
+        if constexpr (here > 0)
+            __builtin_amdgcn_sched_group_barrier(0x100, here, 0);
+        spread_reads<I + 1, N, READS, PER>();
+    }
+}
+
 // Scheduling hint for one k step: alternate its 16 MFMAs with the LDS
 // reads of the next k step (4 A and 8 transposed B reads, or 4 + 4 when W
 // comes transposed).
@@ -136,13 +157,17 @@ __device__ __forceinline__ void interleave_reads_with_mfma()
 {
     constexpr int READS = WT ? T::FM + T::FN : T::FM + 2 * T::FN;
     constexpr int MFMAS = T::FM * T::FN;
-    static_assert(READS <= MFMAS, "one read per MFMA slot at most");
+    if constexpr (READS <= MFMAS) {
 #pragma unroll
-    for (int i = 0; i < READS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        for (int i = 0; i < READS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+    } else {
+        // small wave tiles: more reads than MFMAs, spread over them
+        spread_reads<0, MFMAS, READS, (READS + MFMAS - 1) / MFMAS>();
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
 }
 
 // Swizzle of the B tile: k-row k keeps its 16 chunks of 8 columns, with the
@@ -334,7 +359,8 @@ template <class T, int STAGES, int CPS, int EPI, bool PARK, bool WT>
 __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, TM = T::TM, TN = T::TN, FM = T::FM, FN = T::FN;
-    constexpr int LOADS = T::LOADS, A_BYTES = T::A_BYTES, STAGE_BYTES = T::STAGE_BYTES;
+    constexpr int LOADS_A = T::LOADS_A, LOADS_B = T::LOADS_B;
+    constexpr int A_BYTES = T::A_BYTES, STAGE_BYTES = T::STAGE_BYTES;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int LOG = Log2<CPS>::value;
     constexpr int REG_LEVELS = PARK ? LOG - 1 : LOG;
@@ -367,13 +393,19 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     const i32x4 rb = buffer_desc(wb, b_bytes);
     const uint32_t smem_lds = (uint32_t)(uintptr_t)((DETRED_LDS uint8_t*)smem);
 
-    // Per-lane byte offsets of its LOADS chunks of A and of B inside a block.
-    uint32_t offa[LOADS], offb[LOADS];
+    // Per-lane byte offsets of its LOADS_A chunks of A and LOADS_B chunks of
+    // B inside a block; a wave's load i fills 16-byte slots
+    // (wave * LOADS + i) * 64 + lane of the block.
+    uint32_t offa[LOADS_A], offb[LOADS_B];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int s = (wave * LOADS + i) * 64 + lane;       // 16-byte slot in the stage
+    for (int i = 0; i < LOADS_A; ++i) {
+        const int s = (wave * LOADS_A + i) * 64 + lane;
         const int r = s >> 3, ca = (s & 7) ^ (r & 7);       // A: row r, k-chunk ca
         offa[i] = (uint32_t)((r * g.ldx + 8 * ca) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS_B; ++i) {
+        const int s = (wave * LOADS_B + i) * 64 + lane;
         if (WT) {
             const int n = s >> 3, cn = (s & 7) ^ (n & 7);  // B: row n, k-chunk cn
             offb[i] = (uint32_t)((n * g.ldw + 8 * cn) * 2);
@@ -394,17 +426,16 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     // vector-memory loads per lane.
     auto issue = [&](int t) {
         const int kb = block_k(t);
-        const uint32_t st = smem_lds + (uint32_t)((t % STAGES) * STAGE_BYTES) +
-                            (uint32_t)(wave * LOADS * 1024);
+        const uint32_t st = smem_lds + (uint32_t)((t % STAGES) * STAGE_BYTES);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            dma16(st + i * 1024, offa[i] + (uint32_t)kb * 2, ra);
+        for (int i = 0; i < LOADS_A; ++i)
+            dma16(st + (uint32_t)((wave * LOADS_A + i) * 1024), offa[i] + (uint32_t)kb * 2, ra);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            dma16(st + A_BYTES + i * 1024,
+        for (int i = 0; i < LOADS_B; ++i)
+            dma16(st + (uint32_t)(A_BYTES + (wave * LOADS_B + i) * 1024),
                   offb[i] + (WT ? (uint32_t)kb * 2 : (uint32_t)kb * ldw_bytes), rb);
     };
-    constexpr int LOADS_PER_ISSUE = 2 * LOADS;
+    constexpr int LOADS_PER_ISSUE = LOADS_A + LOADS_B;
 
     // Fragment addresses inside a stage.  A: row r = wm*TM + fm*16 + lane%16,
     // k-chunk 4*ks + lane/16, swizzled by r%8 (= lane%8).  B: lane j of each
@@ -543,9 +574,16 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
 // repeated calls whose weights stay in the MALL.
 template <class T, int CPS>
 struct Stages {
-    static constexpr bool park = (CPS == 8);
-    static constexpr int fit = (DETRED_LDS_STAGES * T::STAGE_BYTES + 16 <= 160 * 1024)
-                                   ? DETRED_LDS_STAGES : 2;
+    // the top level is parked where four copies of a wave's accumulators
+    // would not fit in registers
+    static constexpr bool park = (CPS == 8) && (T::FM * T::FN >= 8);
+    // 32-row tiles: four stages for one-chunk slices (their k-loops are
+    // short, so the prologue's depth is most of the latency cover), two
+    // otherwise (one row of 4096x4096 at 8 slices, weights from HBM: 15.7 /
+    // 14.3 / 14.2 us with 2 / 3 / 4 stages; 14336x4096 at 4 slices: 26.8 /
+    // 28.6 / 30.5 us)
+    static constexpr int want = T::BM == 32 ? (CPS == 1 ? 4 : 2) : DETRED_LDS_STAGES;
+    static constexpr int fit = (want * T::STAGE_BYTES + 16 <= 160 * 1024) ? want : 2;
     static constexpr int value = park ? 3 : fit;
 };
 
@@ -568,22 +606,19 @@ hipError_t launch(const GemmArgs& g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int EPI, bool WT>
+// T1: the tile of one-chunk slices; T: the tile of the others.
+template <class T1, class T, int EPI, bool WT>
 hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
 {
     switch (cps) {
-    case 1:
-        if constexpr (EPI == EPI_STORE)
-            return launch<Tile128x4, 1, EPI, WT>(g, s);
-        else
-            return launch<Tile128, 1, EPI, WT>(g, s);
-    case 2: return launch<Tile128, 2, EPI, WT>(g, s);
-    case 4: return launch<Tile128, 4, EPI, WT>(g, s);
+    case 1: return launch<T1, 1, EPI, WT>(g, s);
+    case 2: return launch<T, 2, EPI, WT>(g, s);
+    case 4: return launch<T, 4, EPI, WT>(g, s);
     case 8:
         if constexpr (EPI == EPI_COMBINE)
             return hipErrorInvalidValue;
         else
-            return launch<Tile128, 8, EPI, WT>(g, s);
+            return launch<T, 8, EPI, WT>(g, s);
     }
     return hipErrorInvalidValue;
 }
@@ -598,7 +633,12 @@ hipError_t launch_layout(int tile, const GemmArgs& g, int cps, hipStream_t s)
         if constexpr (EPI == EPI_STORE)
             return g.wt ? launch<Tile256, 1, EPI, true>(g, s) : launch<Tile256, 1, EPI, false>(g, s);
     }
-    return g.wt ? launch_cps<EPI, true>(g, cps, s) : launch_cps<EPI, false>(g, cps, s);
+    if (tile == TILE_D32)
+        return g.wt ? launch_cps<TileD32, TileD32, EPI, true>(g, cps, s)
+                    : launch_cps<TileD32, TileD32, EPI, false>(g, cps, s);
+    using T1 = std::conditional_t<EPI == EPI_STORE, Tile128x4, Tile128>;
+    return g.wt ? launch_cps<T1, Tile128, EPI, true>(g, cps, s)
+                : launch_cps<T1, Tile128, EPI, false>(g, cps, s);
 }
 
 }  // namespace lds
@@ -608,12 +648,14 @@ bool lds_engine_supports(int tile, const GemmArgs& g, int cps)
     // every MFMA step inside K, and byte offsets of the tile's X rows, W
     // columns and output rows within the 31-bit record range of a buffer
     // descriptor; the 256x256 tile for one-chunk slices only
-    if (g.Kc % 32 != 0 || (tile != TILE_L128 && tile != TILE_L256))
+    if (g.Kc % 32 != 0 || (tile != TILE_L128 && tile != TILE_L256 && tile != TILE_D32))
         return false;
     if (tile == TILE_L256 && cps != 1)
         return false;
-    const size_t BM = tile == TILE_L256 ? lds::Tile256::BM : lds::Tile128::BM;
-    const size_t BN = tile == TILE_L256 ? lds::Tile256::BN : lds::Tile128::BN;
+    const size_t BM = tile == TILE_L256 ? lds::Tile256::BM
+                      : tile == TILE_D32 ? lds::TileD32::BM : lds::Tile128::BM;
+    const size_t BN = tile == TILE_L256 ? lds::Tile256::BN
+                      : tile == TILE_D32 ? lds::TileD32::BN : lds::Tile128::BN;
     const size_t xbytes = ((BM - 1) * g.ldx + g.K) * 2;
     const size_t wbytes = g.wt ? ((BN - 1) * g.ldw + g.K) * 2 : ((size_t)g.K * g.ldw) * 2;
     // output rows of the tile (Y at ldy, partial planes at N, C at ldc)
