@@ -150,20 +150,19 @@ void widen_for_roots(Policy& p, GemmArgs& g, int cps)
     g = w;
 }
 
-// Products of at most 32 rows on the 32x128 tile: the same tile count as
+// Products of at most 64 rows on the 64x128 tile: the same tile count as
 // 128x128 (one tile row either way, so the split, the workspace and the
-// arrival counters are unchanged), but a quarter of the A block, so four
-// stages of weights are in flight instead of two.  The tile never changes
-// the bits.
+// arrival counters are unchanged), but half the A block, so more stages of
+// weights are in flight.  The tile never changes the bits.
 void narrow_for_decode(Policy& p, GemmArgs& g, int cps)
 {
-    if (p.tile != TILE_L128 || g.M > 32)
+    if (p.tile != TILE_L128 || g.M > 64)
         return;
     GemmArgs w = g;
     w.tiles_m = 1;
-    if (!lds_engine_supports(TILE_D32, w, cps))
+    if (!lds_engine_supports(TILE_D64, w, cps))
         return;
-    p.tile = TILE_D32;
+    p.tile = TILE_D64;
     tile_shape(p.tile, &p.bm, &p.bn);
     g = w;
 }

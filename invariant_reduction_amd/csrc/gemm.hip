@@ -397,17 +397,17 @@ void tile_shape(int tile, int* bm, int* bn)
     case TILE_S16: *bm = TileS16::BM; *bn = TileS16::BN; return;
     case TILE_M64: *bm = TileM64::BM; *bn = TileM64::BN; return;
     case TILE_L256: *bm = 256; *bn = 256; return;
-    case TILE_D32: *bm = 32; *bn = 128; return;
+    case TILE_D64: *bm = 64; *bn = 128; return;
     default: *bm = TileL128::BM; *bn = TileL128::BN; return;
     }
 }
 
 hipError_t launch_slice_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s)
 {
-    if ((tile == TILE_L128 || tile == TILE_L256 || tile == TILE_D32) &&
+    if ((tile == TILE_L128 || tile == TILE_L256 || tile == TILE_D64) &&
         lds_engine_supports(tile, g, cps))
         return launch_lds_gemm(tile, epi, g, cps, s);
-    if (tile == TILE_L256 || tile == TILE_D32)
+    if (tile == TILE_L256 || tile == TILE_D64)
         return hipErrorInvalidValue;
     return launch_reg_gemm(tile, epi, g, cps, s);
 }

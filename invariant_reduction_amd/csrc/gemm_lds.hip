@@ -1,8 +1,8 @@
 // LDS-DMA slice GEMM engine for gfx950: the wide-output workgroup tiles,
 // 128x128 (eight waves of 64x32, any chunk count; four of 64x64 for
 // one-chunk root stores), 256x256 (eight waves of 128x64, one-chunk slices
-// only: its accumulators leave no registers for a subtree) and 32x128 for
-// products of at most 32 rows (four waves of 32x32).  Same reduction order, output values and last-arriver combine
+// only: its accumulators leave no registers for a subtree) and 64x128 for
+// products of at most 64 rows (eight waves of 32x32).  Same reduction order, output values and last-arriver combine
 // as the register-staged engine (gemm_common.h); the data movement differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
@@ -75,9 +75,12 @@ using Tile128 = LdsTile<128, 128, 2, 4>;
 // of 512x8192x8192: 104 vs 112 us; 4096x4096x4096: 238 vs 245 us).
 using Tile128x4 = LdsTile<128, 128, 2, 2>;
 using Tile256 = LdsTile<256, 256, 2, 4>;
-// Products of at most 32 rows (decode): 32x128, four waves of 32x32.  The
-// A block shrinks to 4 KiB, so the LDS holds more weight blocks in flight.
-using TileD32 = LdsTile<32, 128, 1, 4>;
+// Products of at most 64 rows (decode and small batches): 64x128, eight
+// waves of 32x32.  The A block shrinks to 8 KiB, so the LDS holds more
+// weight blocks in flight (64 rows of 4096x14336 at 8 slices, weights from
+// HBM: 41.0 -> 32.6 us against 128x128; a 32x128 tile was no faster
+// below 32 rows).
+using TileD64 = LdsTile<64, 128, 2, 4>;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -577,12 +580,12 @@ struct Stages {
     // the top level is parked where four copies of a wave's accumulators
     // would not fit in registers
     static constexpr bool park = (CPS == 8) && (T::FM * T::FN >= 8);
-    // 32-row tiles: four stages for one-chunk slices (their k-loops are
+    // decode tiles: four stages for one-chunk slices (their k-loops are
     // short, so the prologue's depth is most of the latency cover), two
     // otherwise (one row of 4096x4096 at 8 slices, weights from HBM: 15.7 /
     // 14.3 / 14.2 us with 2 / 3 / 4 stages; 14336x4096 at 4 slices: 26.8 /
     // 28.6 / 30.5 us)
-    static constexpr int want = T::BM == 32 ? (CPS == 1 ? 4 : 2) : DETRED_LDS_STAGES;
+    static constexpr int want = T::BM == 64 ? (CPS == 1 ? 4 : 2) : DETRED_LDS_STAGES;
     static constexpr int fit = (want * T::STAGE_BYTES + 16 <= 160 * 1024) ? want : 2;
     static constexpr int value = park ? 3 : fit;
 };
@@ -633,9 +636,9 @@ hipError_t launch_layout(int tile, const GemmArgs& g, int cps, hipStream_t s)
         if constexpr (EPI == EPI_STORE)
             return g.wt ? launch<Tile256, 1, EPI, true>(g, s) : launch<Tile256, 1, EPI, false>(g, s);
     }
-    if (tile == TILE_D32)
-        return g.wt ? launch_cps<TileD32, TileD32, EPI, true>(g, cps, s)
-                    : launch_cps<TileD32, TileD32, EPI, false>(g, cps, s);
+    if (tile == TILE_D64)
+        return g.wt ? launch_cps<TileD64, TileD64, EPI, true>(g, cps, s)
+                    : launch_cps<TileD64, TileD64, EPI, false>(g, cps, s);
     using T1 = std::conditional_t<EPI == EPI_STORE, Tile128x4, Tile128>;
     return g.wt ? launch_cps<T1, Tile128, EPI, true>(g, cps, s)
                 : launch_cps<T1, Tile128, EPI, false>(g, cps, s);
@@ -648,14 +651,14 @@ bool lds_engine_supports(int tile, const GemmArgs& g, int cps)
     // every MFMA step inside K, and byte offsets of the tile's X rows, W
     // columns and output rows within the 31-bit record range of a buffer
     // descriptor; the 256x256 tile for one-chunk slices only
-    if (g.Kc % 32 != 0 || (tile != TILE_L128 && tile != TILE_L256 && tile != TILE_D32))
+    if (g.Kc % 32 != 0 || (tile != TILE_L128 && tile != TILE_L256 && tile != TILE_D64))
         return false;
     if (tile == TILE_L256 && cps != 1)
         return false;
     const size_t BM = tile == TILE_L256 ? lds::Tile256::BM
-                      : tile == TILE_D32 ? lds::TileD32::BM : lds::Tile128::BM;
+                      : tile == TILE_D64 ? lds::TileD64::BM : lds::Tile128::BM;
     const size_t BN = tile == TILE_L256 ? lds::Tile256::BN
-                      : tile == TILE_D32 ? lds::TileD32::BN : lds::Tile128::BN;
+                      : tile == TILE_D64 ? lds::TileD64::BN : lds::Tile128::BN;
     const size_t xbytes = ((BM - 1) * g.ldx + g.K) * 2;
     const size_t wbytes = g.wt ? ((BN - 1) * g.ldw + g.K) * 2 : ((size_t)g.K * g.ldw) * 2;
     // output rows of the tile (Y at ldy, partial planes at N, C at ldc)

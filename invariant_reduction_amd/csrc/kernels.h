@@ -7,7 +7,7 @@
 namespace detred {
 
 enum { EPI_STORE = 0, EPI_COMBINE = 1, EPI_ATOMIC = 2 };
-enum { TILE_S16 = 0, TILE_M64 = 1, TILE_L128 = 2, TILE_L256 = 3, TILE_D32 = 4 };
+enum { TILE_S16 = 0, TILE_M64 = 1, TILE_L128 = 2, TILE_L256 = 3, TILE_D64 = 4 };
 
 struct GemmArgs {
     const uint16_t* X;
@@ -42,7 +42,7 @@ struct GemmArgs {
 void tile_shape(int tile, int* bm, int* bn);
 // Launch the slice GEMM for a tile family; TILE_L128 uses the LDS-DMA engine
 // whenever it supports the shape, else the register-staged engine; TILE_L256
-// (one-chunk slices storing their roots) and TILE_D32 (at most 32 rows)
+// (one-chunk slices storing their roots) and TILE_D64 (at most 64 rows)
 // exist in the LDS-DMA engine only, and are chosen only where that engine
 // supports the shape.
 hipError_t launch_slice_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s);

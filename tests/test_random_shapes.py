@@ -1,5 +1,5 @@
 """Seeded random shapes through every tile the planner can pick (64x16,
-64x64, the register-staged and LDS-DMA 128x128, 32x128 for at most 32
+64x64, the register-staged and LDS-DMA 128x128, 64x128 for at most 64
 rows, 256x256 for long shard roots), both weight layouts and every split:
 all splits and shard counts give the bits of S = 1, and sampled rows meet
 the oracle's tolerance."""
@@ -35,9 +35,9 @@ def _det(X, W, S, dev):
 
 
 # plus shapes that reach the 256x256 shard-root tile (T = 8, chunks of 1024)
-# and the edges of the 32-row tile
-@pytest.mark.parametrize("M,N,K", _shapes(24, 2024) + [(700, 3000, 8192), (32, 3000, 8192),
-                                                      (33, 264, 8192)])
+# and the edges of the 64-row tile
+@pytest.mark.parametrize("M,N,K", _shapes(24, 2024) + [(700, 3000, 8192), (64, 3000, 8192),
+                                                      (65, 264, 8192), (47, 1000, 2048)])
 def test_random_shape_splits_layouts_and_parity(M, N, K, dev):
     X, W = inputs.dense_inputs(M, K, N, seed=M + 3 * N + 7 * K)
     Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
