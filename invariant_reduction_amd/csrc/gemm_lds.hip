@@ -127,9 +127,6 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, const i3
 #pragma clang diagnostic pop
 }
 
-#ifndef DETRED_LDS_STAGES
-#define DETRED_LDS_STAGES 2
-#endif
 constexpr int SCRATCH_BYTES = 0;
 
 // s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
@@ -569,31 +566,26 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     }
 }
 
-// With 8 chunks per slice the top subtree level is parked in LDS, beside
-// three stages: 96 + 64 KiB, the whole LDS of the CU.  The third stage keeps
-// two weight blocks in flight per workgroup, which is what a product whose
-// weights come from HBM needs (256x14336x4096 with the weights not cached:
-// 67.5 -> 53.4 us, 1024 rows 234 -> 185 us on MI355X), at a few percent on
-// repeated calls whose weights stay in the MALL.
+// Stage counts.  With 8 chunks per slice the top subtree level is parked in
+// LDS where four copies of a wave's accumulators would not fit in registers,
+// beside three stages (see the measurements at launch()).  Otherwise the
+// depth follows the grid: a grid of at most 256 workgroups leaves one per
+// CU, and four stages keep three weight blocks in flight (weights from HBM:
+// 256x4096x4096 at 4 slices 32.0 -> 28.8 us, 256x4096x14336 69.5 -> 54.6
+// us, 1024x1024x8192 48.6 -> 40.7 us on MI355X); a larger grid keeps two,
+// so that two workgroups share each CU (512x4096x4096 at 4 slices: 42 us
+// with two stages, 54 with four).
 template <class T, int CPS>
 struct Stages {
-    // the top level is parked where four copies of a wave's accumulators
-    // would not fit in registers
     static constexpr bool park = (CPS == 8) && (T::FM * T::FN >= 8);
-    // decode tiles: four stages for one-chunk slices (their k-loops are
-    // short, so the prologue's depth is most of the latency cover), two
-    // otherwise (one row of 4096x4096 at 8 slices, weights from HBM: 15.7 /
-    // 14.3 / 14.2 us with 2 / 3 / 4 stages; 14336x4096 at 4 slices: 26.8 /
-    // 28.6 / 30.5 us)
-    static constexpr int want = T::BM == 64 ? (CPS == 1 ? 4 : 2) : DETRED_LDS_STAGES;
-    static constexpr int fit = (want * T::STAGE_BYTES + 16 <= 160 * 1024) ? want : 2;
-    static constexpr int value = park ? 3 : fit;
+    static constexpr int shallow = park ? 3 : 2;
+    static constexpr int deep =
+        (!park && 4 * T::STAGE_BYTES + 16 <= 160 * 1024) ? 4 : shallow;
 };
 
-template <class T, int CPS, int EPI, bool WT>
-hipError_t launch(const GemmArgs& g, hipStream_t s)
+template <class T, int ST, int CPS, int EPI, bool WT>
+hipError_t launch_st(const GemmArgs& g, hipStream_t s)
 {
-    constexpr int ST = Stages<T, CPS>::value;
     constexpr bool PK = Stages<T, CPS>::park;
     auto fn = lds_gemm_kernel<T, ST, CPS, EPI, PK, WT>;
     // + the last-arriver flag of a combine (never with 8 chunks per slice)
@@ -607,6 +599,21 @@ hipError_t launch(const GemmArgs& g, hipStream_t s)
     const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);
     hipLaunchKernelGGL(fn, dim3(grid), dim3(T::THREADS), bytes, s, g);
     return hipGetLastError();
+}
+
+// Eight-chunk slices (parked level, 96 + 64 KiB) keep three stages: two
+// weight blocks in flight per workgroup, which is what a product whose
+// weights come from HBM needs (256x14336x4096 with the weights not cached:
+// 67.5 -> 53.4 us, 1024 rows 234 -> 185 us on MI355X), at a few percent on
+// repeated calls whose weights stay in the MALL.
+template <class T, int CPS, int EPI, bool WT>
+hipError_t launch(const GemmArgs& g, hipStream_t s)
+{
+    using St = Stages<T, CPS>;
+    const long wgs = (long)g.tiles_m * g.tiles_n * g.slices;
+    if (St::deep != St::shallow && wgs <= 256)
+        return launch_st<T, St::deep, CPS, EPI, WT>(g, s);
+    return launch_st<T, St::shallow, CPS, EPI, WT>(g, s);
 }
 
 // T1: the tile of one-chunk slices; T: the tile of the others.
