@@ -335,10 +335,6 @@ LoraLayout lora_layout(int M, int N, int K, int r)
 
 }  // namespace
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
 
 int det_gemm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* Y,
@@ -521,13 +517,8 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     if (ldy == N)
         return hip_status(launch_tree_combine((const float*)ws, (size_t)M * N, T, Y,
                                               (size_t)M * N, hs));
-    for (int r = 0; r < M; ++r) {  // strided output: one combine per row
-        e = launch_tree_combine((const float*)ws + (size_t)r * N, (size_t)M * N, T,
-                                Y + (size_t)r * ldy, (size_t)N, hs);
-        if (e != hipSuccess)
-            return DETRED_EHIP;
-    }
-    return DETRED_OK;
+    return hip_status(
+        launch_tree_combine_rows((const float*)ws, (size_t)M * N, T, N, Y, ldy, M, hs));
 }
 
 int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* P, int M,

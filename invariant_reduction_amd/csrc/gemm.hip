@@ -302,6 +302,35 @@ __global__ __launch_bounds__(256) void tree_combine_kernel(const float* __restri
     }
 }
 
+// The same tree for an output with padded rows: element (r, c) of each
+// part plane at r*N + c, of Y at r*ldy + c; 4 columns per thread.
+template <int COUNT>
+__global__ __launch_bounds__(256) void tree_combine_rows_kernel(const float* __restrict__ parts,
+                                                                size_t stride, int N,
+                                                                float* __restrict__ Y, long ldy,
+                                                                size_t total4)
+{
+    const size_t per_row = (size_t)N / 4;
+    for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < total4;
+         v += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = v / per_row, c = 4 * (v % per_row);
+        float4 vals[COUNT];
+#pragma unroll
+        for (int s = 0; s < COUNT; ++s)
+            vals[s] = *reinterpret_cast<const float4*>(parts + (size_t)s * stride + r * N + c);
+#pragma unroll
+        for (int w = COUNT; w > 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < (w >> 1); ++i) {
+                vals[i].x = vals[2 * i].x + vals[2 * i + 1].x;
+                vals[i].y = vals[2 * i].y + vals[2 * i + 1].y;
+                vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
+                vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
+            }
+        *reinterpret_cast<float4*>(Y + r * ldy + c) = vals[0];
+    }
+}
+
 // Y[r][0..N) = +0 for r < M (row stride ld); N % 4 == 0.
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* Y, long ld, int M, int N)
 {
@@ -440,6 +469,21 @@ hipError_t launch_tree_combine(const float* parts, size_t stride, int count, flo
     case 2: hipLaunchKernelGGL(tree_combine_kernel<2>, grid, block, 0, s, parts, stride, Y, n4); break;
     case 4: hipLaunchKernelGGL(tree_combine_kernel<4>, grid, block, 0, s, parts, stride, Y, n4); break;
     case 8: hipLaunchKernelGGL(tree_combine_kernel<8>, grid, block, 0, s, parts, stride, Y, n4); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_combine_rows(const float* parts, size_t stride, int count, int N, float* Y,
+                                    long ldy, int M, hipStream_t s)
+{
+    const size_t total4 = (size_t)M * (N / 4);
+    const dim3 grid(grid_for(total4, 256)), block(256);
+    switch (count) {
+    case 1: hipLaunchKernelGGL(tree_combine_rows_kernel<1>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
+    case 2: hipLaunchKernelGGL(tree_combine_rows_kernel<2>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
+    case 4: hipLaunchKernelGGL(tree_combine_rows_kernel<4>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
+    case 8: hipLaunchKernelGGL(tree_combine_rows_kernel<8>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -91,6 +91,23 @@ def test_strided_operands(dev):
     assert torch.all(Yt[:, N:] == -7.0)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 264, 2048), (5, 1032, 8192)])
+def test_tree_tp_padded_output(M, N, K, dev):
+    """tree_tp_gemm into rows ldy > N apart: the cross-shard combine walks
+    the padded rows, writes nothing past N and gives det's bits for every T."""
+    X, W = inputs.dense_inputs(M, K, N, seed=M + N)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    ref = torch.empty((M, N), dtype=torch.float32, device=dev)
+    detred.det_splitk_gemm(Xd, Wd, ref, 1, detred.workspace(M, N, K, 1, dev))
+    for T in (2, 4, 8):
+        Yp = torch.full((M, N + 24), -7.0, dtype=torch.float32, device=dev)
+        detred.tree_tp_gemm(Xd, Wd, Yp[:, :N], T, detred.workspace(M, N, K, T, dev))
+        torch.cuda.synchronize()
+        assert_bitwise(Yp[:, :N], ref, "padded tree_tp T=%d vs det" % T)
+        assert torch.all(Yp[:, N:] == -7.0), "wrote past the row"
+    assert_gemm_parity(ref, X, W, rows=[0, M // 2, M - 1])
+
+
 def test_combine_equals_cpu_tree_over_partials(dev):
     """det S=8: Y is exactly the fp32 tree ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))
     over the slice partials left in the workspace (layout: S planes of M*N)."""
