@@ -68,6 +68,26 @@ def test_dense_rows_invariant_across_m(dev):
         assert torch.equal(Y[:M].view(torch.int32), ref[:M].view(torch.int32)), "M=%d" % M
 
 
+@pytest.mark.parametrize("N,K,Ms", [(4096, 4096, (200, 256, 512, 700)),
+                                     (1024, 8192, (1024, 2048, 3000))])
+def test_rows_invariant_across_lds_stage_depth(N, K, Ms, dev):
+    """The 128x128 engine keeps four LDS stages for grids of at most 256
+    workgroups and two above; the automatic split also changes with M.  The
+    shared rows must not notice: here 200, 256 and 1024 rows run 4 slices on
+    256 workgroups (four stages), 512 and 2048 rows 4 slices on 512 (two),
+    and the reference rows run unsplit (three stages beside the parked tree
+    level)."""
+    M = Ms[-1]
+    X, W = inputs.dense_inputs(M, K, N, seed=11)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    ref = det(Xd, Wd, 0, dev)
+    for m in Ms[:-1]:
+        y = det(Xd, Wd, 0, dev, M=m)
+        torch.cuda.synchronize()
+        assert_bitwise(y, ref[:m], "M=%d vs M=%d (split %d vs %d)"
+                       % (m, M, detred.auto_split(m, N, K), detred.auto_split(M, N, K)))
+
+
 def test_position_invariance(dev):
     """f(X[j:j+1])[0] == f(X)[j], and permuting the rows permutes the output."""
     cases = [(256, 64, 4096), (300, 16, 512), (257, 264, 2048)]
