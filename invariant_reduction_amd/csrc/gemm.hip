@@ -376,8 +376,8 @@ static hipError_t launch_t(const GemmArgs& g, hipStream_t s)
 {
     auto fn = slice_gemm_kernel<T, CPS, EPI, WT>;
     constexpr int lds = lds_bytes<T, CPS>();
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    static std::atomic<unsigned long long> lds_set{0};
+    const hipError_t attr = ensure_lds_limit(lds_set, reinterpret_cast<const void*>(fn), lds);
     if (attr != hipSuccess)
         return attr;
     const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);

@@ -592,8 +592,8 @@ hipError_t launch_st(const GemmArgs& g, hipStream_t s)
     constexpr int bytes = ST * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) + SCRATCH_BYTES +
                           (EPI == EPI_COMBINE ? 16 : 0);
     static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    static std::atomic<unsigned long long> lds_set{0};
+    const hipError_t attr = ensure_lds_limit(lds_set, reinterpret_cast<const void*>(fn), bytes);
     if (attr != hipSuccess)
         return attr;
     const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);

@@ -4,7 +4,28 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace detred {
+
+// A kernel's dynamic-LDS limit is raised once per device: `done` (one
+// static per kernel) has bit d set once device d has it.  Devices past 63
+// set it on every launch.
+inline hipError_t ensure_lds_limit(std::atomic<unsigned long long>& done, const void* fn,
+                                   int bytes)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 enum { EPI_STORE = 0, EPI_COMBINE = 1, EPI_ATOMIC = 2 };
 enum { TILE_S16 = 0, TILE_M64 = 1, TILE_L128 = 2, TILE_L256 = 3, TILE_D64 = 4 };

@@ -344,9 +344,9 @@ template <bool MEAN>
 static hipError_t launch_lsm(const float* x, float* y, float* mu, int rows, int cols,
                              hipStream_t s)
 {
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(log_softmax_kernel<MEAN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, LSM_LDS_BYTES);
+    static std::atomic<unsigned long long> lds_set{0};
+    const hipError_t attr = ensure_lds_limit(
+        lds_set, reinterpret_cast<const void*>(log_softmax_kernel<MEAN>), LSM_LDS_BYTES);
     if (attr != hipSuccess)
         return attr;
     hipLaunchKernelGGL(log_softmax_kernel<MEAN>, dim3(rows), dim3(LSM_THREADS), LSM_LDS_BYTES, s,
