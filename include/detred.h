@@ -105,9 +105,12 @@ int detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
  * The split that split_k = 0 selects for an M x N x K product.  The split
  * only decides how many workgroups share the chunk tree; the bits of the
  * result never depend on it (nor on M).  Outputs of at most 64 columns use
- * one slice per chunk (S = P).  Wider ones use S = 1 when their tiles
- * already cover at least 192 CUs, else S = 4, or 8 (<= P) while
- * tiles*S < 256 (two slices are never chosen: they are slower than four).
+ * one slice per chunk (S = P).  For wider ones, with t = the number of
+ * 128 x 128 output tiles and Kc = K / P:
+ *   t <= 128:       the largest S (<= P) with t*S <= 256, but 4 instead of
+ *                   2 for products of at most 16 rows;
+ *   129 <= t < 192: S = 4 if Kc >= 1024, else 1;
+ *   t >= 192:       S = 1, but 4 for 257 <= t <= 447 when Kc >= 1024.
  * Returns 0 for invalid arguments.
  */
 int detred_auto_split(int M, int N, int K);

@@ -169,25 +169,41 @@ void narrow_for_decode(Policy& p, GemmArgs& g, int cps)
 
 // The split for split_k = 0.  The split only decides how many workgroups
 // share the chunk tree, never the bits.  Narrow outputs keep the policy's
-// split (one slice per chunk).  A wide product splits while its output tiles
-// leave CUs idle: S = 1 once the tiles cover 192 CUs (there the extra
-// partial traffic costs more than the idle CUs), else S = 4, or 8 while
-// tiles*S < 256.  Two slices of four chunks are never the fastest: with the
-// weights coming from HBM, 512x4096x14336 takes 113 / 89 us at S = 2 / 4,
-// 512x4096x4096 44 / 42 us, 2048x1024x8192 72 / 61 us on MI355X.  Chosen
-// from timings of 1..2048-row products with N in {1024, 4096, 8192, 14336}
-// and K in {4096, 8192, 14336}.
+// split (one slice per chunk).  A wide product is sized against the 256 CUs
+// and the LDS engine's stage depth (four stages for a grid of at most 256
+// workgroups, two above):
+//  - fewer than 129 output tiles: the most slices that keep the grid at
+//    or under 256 workgroups (so four stages), except that products of at
+//    most 16 rows take 4 slices rather than 2;
+//  - 129..191 tiles: unsplit when chunks are short (below 1024), else 4
+//    slices;
+//  - 192 or more: unsplit, except 4 slices for 257..447 tiles with chunks
+//    of 1024 or more (an unsplit grid of 1.0-1.75 waves of workgroups
+//    leaves CUs idle through a long K).
+// Measured on MI355X with the weights coming from HBM over M in 1..2560,
+// N in {1024..14336}, K in {4096, 8192, 14336}: e.g. 128x14336x4096 45.2 ->
+// 38.2 us (2 slices, not 4), 768x1024x4096 33.5 -> 29.2 us (4, not 8),
+// 384x14336x8192 171 -> 149 us (4, not 1), 640x4096x4096 56 -> 53 us (1,
+// not 4).
 int auto_split(const Policy& p, int M, int N)
 {
     if (p.tile != TILE_L128)
         return p.default_split;
     const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-    if (tiles >= 192)
-        return 1;
-    int S = p.P < 4 ? p.P : 4;
-    while (S < p.P && tiles * S < 256)
-        S *= 2;
-    return S;
+    const bool long_chunks = p.Kc >= 1024;
+    int S = 1;
+    if (tiles >= 192) {
+        if (long_chunks && tiles > 256 && tiles < 448)
+            S = 4;
+    } else if (tiles > 128) {
+        S = long_chunks ? 4 : 1;
+    } else {
+        while (S < p.P && tiles * S * 2 <= 256)
+            S *= 2;
+        if (S == 2 && M <= 16)
+            S = 4;
+    }
+    return S < p.P ? S : p.P;
 }
 
 // Resolve split_k / tp_shards against the policy; 0 means auto_split.

@@ -56,12 +56,22 @@ def test_policy_is_locked_by_n_and_k():
 
 
 def test_auto_split():
-    # wide outputs split while their 128 x 128 tiles leave CUs idle
+    # wide outputs: the most slices that keep the grid at <= 256 workgroups
+    # below 129 tiles, unsplit from 192 tiles, 4 slices between with long
+    # chunks and for 257..447 tiles with long chunks
     assert detred.auto_split(256, 14336, 4096) == 1      # 224 tiles
-    assert detred.auto_split(1, 14336, 4096) == 4        # 112 tiles
+    assert detred.auto_split(1, 14336, 4096) == 4        # 112 tiles, at most 16 rows
+    assert detred.auto_split(32, 14336, 4096) == 2       # 112 tiles
+    assert detred.auto_split(128, 14336, 4096) == 2      # 112 tiles
     assert detred.auto_split(256, 4096, 4096) == 4       # 64 tiles
-    assert detred.auto_split(512, 4096, 4096) == 4       # 128 tiles: two slices are skipped
+    assert detred.auto_split(512, 4096, 4096) == 2       # 128 tiles
+    assert detred.auto_split(768, 1024, 4096) == 4       # 48 tiles
     assert detred.auto_split(1, 1024, 4096) == 8         # 8 tiles, capped at P
+    assert detred.auto_split(640, 4096, 4096) == 1       # 160 tiles, chunks of 512
+    assert detred.auto_split(640, 4096, 8192) == 4       # 160 tiles, chunks of 1024
+    assert detred.auto_split(384, 14336, 8192) == 4      # 336 tiles, chunks of 1024
+    assert detred.auto_split(384, 14336, 4096) == 1      # 336 tiles, chunks of 512
+    assert detred.auto_split(512, 14336, 8192) == 1      # 448 tiles
     assert detred.auto_split(1024, 4096, 4096) == 1      # 256 tiles
     assert detred.auto_split(1, 4096, 64) == 1           # one chunk
     assert detred.auto_split(4096, 64, 4096) == 8        # narrow: one slice per chunk
