@@ -574,7 +574,10 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
 // 256x4096x4096 at 4 slices 32.0 -> 28.8 us, 256x4096x14336 69.5 -> 54.6
 // us, 1024x1024x8192 48.6 -> 40.7 us on MI355X); a larger grid keeps two,
 // so that two workgroups share each CU (512x4096x4096 at 4 slices: 42 us
-// with two stages, 54 with four).
+// with two stages, 54 with four), unless the kernel's registers leave room
+// for only one workgroup per CU anyway (four chunks per slice on 128x128):
+// then it takes four (1024x8192x8192 at 2 slices, weights from HBM: 266 ->
+// 217 us).
 template <class T, int CPS>
 struct Stages {
     static constexpr bool park = (CPS == 8) && (T::FM * T::FN >= 8);
@@ -610,9 +613,25 @@ template <class T, int CPS, int EPI, bool WT>
 hipError_t launch(const GemmArgs& g, hipStream_t s)
 {
     using St = Stages<T, CPS>;
-    const long wgs = (long)g.tiles_m * g.tiles_n * g.slices;
-    if (St::deep != St::shallow && wgs <= 256)
-        return launch_st<T, St::deep, CPS, EPI, WT>(g, s);
+    if constexpr (St::deep != St::shallow) {
+        // Deep also where a CU holds only one workgroup of the shallow form
+        // anyway (its registers allow no second one): the extra stages then
+        // cost no occupancy.
+        static const int per_cu = [] {
+            constexpr bool PK = St::park;
+            constexpr int bytes = St::shallow * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) +
+                                  SCRATCH_BYTES + (EPI == EPI_COMBINE ? 16 : 0);
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, lds_gemm_kernel<T, St::shallow, CPS, EPI, PK, WT>, T::THREADS, bytes) !=
+                hipSuccess)
+                n = 0;
+            return n;
+        }();
+        const long wgs = (long)g.tiles_m * g.tiles_n * g.slices;
+        if (wgs <= 256 || per_cu == 1)
+            return launch_st<T, St::deep, CPS, EPI, WT>(g, s);
+    }
     return launch_st<T, St::shallow, CPS, EPI, WT>(g, s);
 }
 
