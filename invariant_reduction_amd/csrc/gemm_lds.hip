@@ -2,11 +2,13 @@
 // 128x128 (eight waves of 64x32, any chunk count; four of 64x64 for
 // one-chunk root stores), 256x256 (eight waves of 128x64, one-chunk slices
 // only: its accumulators leave no registers for a subtree) and 64x128 for
-// products of at most 64 rows (eight waves of 32x32).  Same reduction order, output values and last-arriver combine
-// as the register-staged engine (gemm_common.h); the data movement differs:
+// products of at most 64 rows (eight waves of 32x32).  Same reduction
+// order, output values and last-arriver combine as the register-staged
+// engine (gemm_common.h); the data movement differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
-//    STAGES K blocks of 64 in flight; the buffer descriptors' record counts
+//    STAGES K blocks of 64 in flight (two to four, see Stages); the
+//    buffer descriptors' record counts
 //    turn rows past M into zeros.  These loads are issued from inline
 //    assembly (they have no register result) and waited for explicitly with
 //    s_waitcnt vmcnt + s_barrier: issued through the compiler builtin, they
