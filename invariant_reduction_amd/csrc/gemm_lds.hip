@@ -8,8 +8,8 @@
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
 //    STAGES K blocks of 64 in flight (two to four, see Stages); the
-//    buffer descriptors' record counts
-//    turn rows past M into zeros.  These loads are issued from inline
+//    buffer descriptors' record counts turn rows past M into zeros.  These
+//    loads are issued from inline
 //    assembly (they have no register result) and waited for explicitly with
 //    s_waitcnt vmcnt + s_barrier: issued through the compiler builtin, they
 //    make every later ds_read_b64_tr_b16 wait for all outstanding loads,
