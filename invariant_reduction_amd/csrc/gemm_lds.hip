@@ -9,11 +9,10 @@
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
 //    STAGES K blocks of 64 in flight (two to four, see Stages); the
 //    buffer descriptors' record counts turn rows past M into zeros.  These
-//    loads are issued from inline
-//    assembly (they have no register result) and waited for explicitly with
-//    s_waitcnt vmcnt + s_barrier: issued through the compiler builtin, they
-//    make every later ds_read_b64_tr_b16 wait for all outstanding loads,
-//    which would leave one stage in flight;
+//    loads are issued from inline assembly (they have no register result)
+//    and waited for explicitly with s_waitcnt vmcnt + s_barrier: issued
+//    through the compiler builtin, they make every later ds_read_b64_tr_b16
+//    wait for all outstanding loads, which would leave one stage in flight;
 //  * A (X, K-contiguous) is stored [m][k] and read as one 16-byte
 //    ds_read_b128 per MFMA operand;
 //  * B (W, N-contiguous) is stored [k][n] as loaded and read with
