@@ -152,3 +152,52 @@ def test_log_softmax_mean_fused_equals_separate(B, V, dev):
     assert_bitwise(fm, ym, "fused mean")
     assert_bitwise(xi, yl, "fused in place")
     assert_bitwise(mi, ym, "fused mean, in place")
+
+
+def test_logit_ops_full_batch_sampled_rows(dev):
+    """The full logits batch [4096, 151936] through the one-pass call, as the
+    benchmark runs it: sampled rows meet the oracle, and each equals the
+    same row computed alone."""
+    B, V = 4096, 151936
+    x = inputs.logits_inputs(B, V, seed=21)
+    xd = dev_f32(x, dev)
+    y = torch.empty_like(xd)
+    mu = torch.empty(B, dtype=torch.float32, device=dev)
+    detred.inv_log_softmax_mean(xd, y, mu)
+    rows = [0, 1, 777, 2048, 4095]
+    yh = host(y[rows]).astype(np.float64)
+    xs = x[rows]
+    ref = oracle.log_softmax(xs)
+    assert np.all(np.abs(yh - ref) <= lsm_tol(xs, ref))
+    tol = 1e-5 * np.abs(xs.astype(np.float64)).sum(axis=1) / V + 1e-6
+    assert np.all(np.abs(host(mu[rows]).astype(np.float64) - oracle.mean(xs)) <= tol)
+    for j in rows:
+        y1 = torch.empty((1, V), dtype=torch.float32, device=dev)
+        m1 = torch.empty(1, dtype=torch.float32, device=dev)
+        detred.inv_log_softmax_mean(xd[j:j + 1], y1, m1)
+        torch.cuda.synchronize()
+        assert_bitwise(y1[0], y[j], "row %d alone vs in the batch" % j)
+        assert_bitwise(m1[0], mu[j], "mean of row %d alone vs in the batch" % j)
+
+
+@pytest.mark.parametrize("V", [262144, 1000004])
+def test_logit_ops_rows_wider_than_the_cache(V, dev):
+    """Rows longer than the part kept on chip between the two passes: the
+    rest is streamed twice; parity and fused == separate still hold."""
+    B = 2
+    x = inputs.logits_inputs(B, V, seed=V)
+    xd = dev_f32(x, dev)
+    yl = torch.empty_like(xd)
+    ym = torch.empty(B, dtype=torch.float32, device=dev)
+    detred.inv_log_softmax(xd, yl)
+    detred.inv_mean(xd, ym)
+    fl = torch.empty_like(xd)
+    fm = torch.empty(B, dtype=torch.float32, device=dev)
+    detred.inv_log_softmax_mean(xd, fl, fm)
+    torch.cuda.synchronize()
+    ref = oracle.log_softmax(x)
+    assert np.all(np.abs(host(yl).astype(np.float64) - ref) <= lsm_tol(x, ref))
+    tol = 1e-5 * np.abs(x.astype(np.float64)).sum(axis=1) / V + 1e-6
+    assert np.all(np.abs(host(ym).astype(np.float64) - oracle.mean(x)) <= tol)
+    assert_bitwise(fl, yl, "fused log_softmax, V=%d" % V)
+    assert_bitwise(fm, ym, "fused mean, V=%d" % V)
