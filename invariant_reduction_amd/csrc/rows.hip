@@ -56,6 +56,10 @@ __device__ __forceinline__ float block_sum(float v, float* red)
 
 // ------------------------------------------------------------------ RMSNorm
 constexpr int RMS_THREADS = 256;
+// 16-byte vectors per thread kept in registers between RMSNorm's two passes
+// (repeated 4096x4096: 21.6 -> 20.3 us, with x coming from HBM 26.0 -> 24.4
+// us on MI355X)
+constexpr int RMS_KEEP = 4;
 
 // OutT float: fp32 output; OutT uint16_t: the same fp32 values rounded to
 // bf16 (nearest even) as they are stored.
@@ -70,9 +74,11 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * hidden);
     const int nv = hidden / 8;
 
+    // A thread's first RMS_KEEP vectors (the whole row up to 8192 wide) stay
+    // in registers for the second pass; the rest is read again.
+    uint4 keep[RMS_KEEP];
     float ss = 0.0f;
-    for (int v = threadIdx.x; v < nv; v += RMS_THREADS) {
-        const uint4 q = xr[v];
+    auto square_sum = [&](const uint4 q) {
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -80,13 +86,24 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
             ss = ss + a * a;
             ss = ss + b * b;
         }
+    };
+#pragma unroll
+    for (int i = 0; i < RMS_KEEP; ++i) {
+        const int v = threadIdx.x + i * RMS_THREADS;
+        keep[i] = v < nv ? xr[v] : make_uint4(0u, 0u, 0u, 0u);
     }
+#pragma unroll
+    for (int i = 0; i < RMS_KEEP; ++i)
+        if (threadIdx.x + i * RMS_THREADS < nv)
+            square_sum(keep[i]);
+    for (int v = threadIdx.x + RMS_KEEP * RMS_THREADS; v < nv; v += RMS_THREADS)
+        square_sum(xr[v]);
     ss = block_sum<RMS_THREADS / 64>(ss, red);
     const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
 
     const uint4* gr = reinterpret_cast<const uint4*>(gamma);
-    for (int v = threadIdx.x; v < nv; v += RMS_THREADS) {
-        const uint4 q = xr[v], gq = gr[v];
+    auto emit = [&](int v, const uint4 q) {
+        const uint4 gq = gr[v];
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
         const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w};
         float o[8];
@@ -107,7 +124,15 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(const uint16_t* __
             b.w = f32_to_bf16_bits(o[6]) | (f32_to_bf16_bits(o[7]) << 16);
             reinterpret_cast<uint4*>(y + row * hidden)[v] = b;
         }
+    };
+#pragma unroll
+    for (int i = 0; i < RMS_KEEP; ++i) {
+        const int v = threadIdx.x + i * RMS_THREADS;
+        if (v < nv)
+            emit(v, keep[i]);
     }
+    for (int v = threadIdx.x + RMS_KEEP * RMS_THREADS; v < nv; v += RMS_THREADS)
+        emit(v, xr[v]);
 }
 
 // -------------------------------------------------------------- log_softmax
