@@ -137,10 +137,13 @@ int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
  * Deterministic split-K product Y[M,N] (fp32) = X[M,K] W[K,N] (bf16), the
  * fixed-order split-K of the split-K paper (Highlights, Q&A) with the
  * canonical tree above.  split_k = S in {1,2,4,8} (S <= P), or 0 for
- * detred_auto_split(M, N, K).  With S > 1 each slice writes its fp32 partial into the
- * workspace as S row-major [M][N] arrays (ld N) at byte offset 0, the last
- * slice of every output tile to finish adds the S partials in the fixed tree
- * order and writes Y; one launch in total.  ws may be NULL when S == 1.
+ * detred_auto_split(M, N, K).  With S > 1 each slice writes its fp32
+ * subtree root into the workspace as S row-major [M][N] arrays (ld N) at
+ * byte offset 0, and the top log2(S) levels of the tree add them into Y:
+ * in a second launch that streams over the S arrays when N > 64 or
+ * M*N >= 16384, otherwise (small narrow outputs) by the last slice of each
+ * output tile to finish, in the same launch.  Either way the bits are the
+ * same.  ws may be NULL when S == 1.
  * ws must be 256-byte aligned and at least detred_gemm_workspace_bytes()
  * large (EWORKSPACE otherwise), and its counters zero (detred_workspace_init).
  * With S > 1, N must stay below about 4.1 million (the combine addresses a
@@ -165,8 +168,8 @@ int det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * C is fp32, 16-byte aligned; ldc = 0 broadcasts one row of N values (a
  * bias) to every row, otherwise ldc >= N and ldc % 4 == 0.  Y is 16-byte
  * aligned, ldy % 4 == 0, in elements of y_dtype.  The epilogue is applied
- * where the final value of an element is written (after the tree combine
- * when split_k > 1), so it adds no pass over Y.  split_k, ws and errors as
+ * where the final value of an element is written (in the tree combine when
+ * split_k > 1), so it adds no pass over Y.  split_k, ws and errors as
  * det_splitk_gemm; EINVAL for a bad y_dtype, C or ldc.  K == 0 gives
  * y = beta*C + alpha*(+0).  Row i of Y depends only on row i of X (and of C).
  */

@@ -302,22 +302,22 @@ __global__ __launch_bounds__(256) void tree_combine_kernel(const float* __restri
     }
 }
 
-// The same tree for an output with padded rows: element (r, c) of each
-// part plane at r*N + c, of Y at r*ldy + c; 4 columns per thread.
+// The same tree into g.Y with its row stride and, when g.epi, the addmm
+// epilogue (beta*C + alpha*p, fp32 or bf16) applied to the combined value:
+// element (r, c) of each part plane at r*N + c; 4 columns per thread.
 template <int COUNT>
 __global__ __launch_bounds__(256) void tree_combine_rows_kernel(const float* __restrict__ parts,
-                                                                size_t stride, int N,
-                                                                float* __restrict__ Y, long ldy,
-                                                                size_t total4)
+                                                                size_t stride, GemmArgs g)
 {
-    const size_t per_row = (size_t)N / 4;
+    const size_t per_row = (size_t)g.N / 4;
+    const size_t total4 = per_row * (size_t)g.M;
     for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < total4;
          v += (size_t)gridDim.x * blockDim.x) {
         const size_t r = v / per_row, c = 4 * (v % per_row);
         float4 vals[COUNT];
 #pragma unroll
         for (int s = 0; s < COUNT; ++s)
-            vals[s] = *reinterpret_cast<const float4*>(parts + (size_t)s * stride + r * N + c);
+            vals[s] = *reinterpret_cast<const float4*>(parts + (size_t)s * stride + r * g.N + c);
 #pragma unroll
         for (int w = COUNT; w > 1; w >>= 1)
 #pragma unroll
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void tree_combine_rows_kernel(const float* __r
                 vals[i].z = vals[2 * i].z + vals[2 * i + 1].z;
                 vals[i].w = vals[2 * i].w + vals[2 * i + 1].w;
             }
-        *reinterpret_cast<float4*>(Y + r * ldy + c) = vals[0];
+        write_final4(g, (int)r, (int)c, vals[0]);
     }
 }
 
@@ -474,16 +474,16 @@ hipError_t launch_tree_combine(const float* parts, size_t stride, int count, flo
     return hipGetLastError();
 }
 
-hipError_t launch_tree_combine_rows(const float* parts, size_t stride, int count, int N, float* Y,
-                                    long ldy, int M, hipStream_t s)
+hipError_t launch_tree_combine_rows(const float* parts, size_t stride, int count,
+                                    const GemmArgs& g, hipStream_t s)
 {
-    const size_t total4 = (size_t)M * (N / 4);
+    const size_t total4 = (size_t)g.M * (g.N / 4);
     const dim3 grid(grid_for(total4, 256)), block(256);
     switch (count) {
-    case 1: hipLaunchKernelGGL(tree_combine_rows_kernel<1>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
-    case 2: hipLaunchKernelGGL(tree_combine_rows_kernel<2>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
-    case 4: hipLaunchKernelGGL(tree_combine_rows_kernel<4>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
-    case 8: hipLaunchKernelGGL(tree_combine_rows_kernel<8>, grid, block, 0, s, parts, stride, N, Y, ldy, total4); break;
+    case 1: hipLaunchKernelGGL(tree_combine_rows_kernel<1>, grid, block, 0, s, parts, stride, g); break;
+    case 2: hipLaunchKernelGGL(tree_combine_rows_kernel<2>, grid, block, 0, s, parts, stride, g); break;
+    case 4: hipLaunchKernelGGL(tree_combine_rows_kernel<4>, grid, block, 0, s, parts, stride, g); break;
+    case 8: hipLaunchKernelGGL(tree_combine_rows_kernel<8>, grid, block, 0, s, parts, stride, g); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -3,8 +3,10 @@
 // one-chunk root stores), 256x256 (eight waves of 128x64, one-chunk slices
 // only: its accumulators leave no registers for a subtree) and 64x128 for
 // products of at most 64 rows (eight waves of 32x32).  Same reduction
-// order, output values and last-arriver combine as the register-staged
-// engine (gemm_common.h); the data movement differs:
+// order and output values as the register-staged engine (gemm_common.h);
+// split products on these tiles write their subtree roots and are
+// combined by a second launch, so no last-arriver combine lives here.  The
+// data movement differs:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds (no register staging),
 //    STAGES K blocks of 64 in flight (two to four, see Stages); the
@@ -128,7 +130,6 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, const i3
 #pragma clang diagnostic pop
 }
 
-constexpr int SCRATCH_BYTES = 0;
 
 // s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
 __device__ __forceinline__ void wait_lgkmcnt0()
@@ -232,12 +233,10 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[T::FM][T::FN], const bf16x
 // then every thread stores whole 16-byte row pieces.  A tile larger than
 // the stage buffers goes in PASSES row halves, each written by the waves
 // that own those rows.
-// COHERENT: device-coherent (sc1) buffer stores, for partials that another
-// workgroup combines; shard roots (several planes, out_z_stride set) with
-// plain stores, as the cross-shard combine reads them next; final outputs
-// non-temporal (kept in the caches, a large output pushes out the operands
-// still being read).
-template <class T, int STAGES, bool COHERENT>
+// Subtree roots (several planes, out_z_stride set) go out with plain
+// stores, as the combine reads them next; final outputs non-temporally (a
+// large output would push out the operands still being read).
+template <class T, int STAGES>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::FN],
                                                    const GemmArgs& g, float* out, int ld, int row0,
                                                    int col0, int wm, int wn, int lane, int tid,
@@ -288,7 +287,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::
                 const int r = v / (BN / 4), c4 = v % (BN / 4);
                 val[i] = *reinterpret_cast<const u32x4*>(t + r * BN + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
             }
-            if (COHERENT || !g.epi) {
+            if (!g.epi) {
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     out + (size_t)prow0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
                 auto put = [&](auto policy) {
@@ -302,9 +301,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::
                                                                decltype(policy)::value);
                     }
                 };
-                if (COHERENT)
-                    put(std::integral_constant<int, CPOL_SC1>());
-                else if (g.out_z_stride)
+                if (g.out_z_stride)
                     put(std::integral_constant<int, 0>());
                 else
                     put(std::integral_constant<int, CPOL_NT>());
@@ -365,7 +362,6 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int LOG = Log2<CPS>::value;
     constexpr int REG_LEVELS = PARK ? LOG - 1 : LOG;
-    constexpr int scratch_offset = STAGES * STAGE_BYTES + (PARK ? T::PARK_BYTES : 0);
     constexpr int NSTK = REG_LEVELS > 0 ? REG_LEVELS : 1;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -549,21 +545,10 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     if constexpr (EPI == EPI_ATOMIC) {
         store_tile<FM, FN>(acc, g.Y, g.ldy, g.M, g.N, wrow0, wcol0, lane, true);
     } else {
-        float* out;
-        int ld;
-        if constexpr (EPI == EPI_STORE) {
-            out = g.Y + (size_t)tc.z * g.out_z_stride;
-            ld = g.ldy;
-        } else {
-            out = g.part + (size_t)tc.z * g.M * g.N;
-            ld = g.N;
-        }
-        store_tile_via_lds<T, STAGES, EPI == EPI_COMBINE>(acc, g, out, ld, row0, col0, wm, wn,
-                                                          lane, tid, smem);
-        if constexpr (EPI == EPI_COMBINE) {
-            int* s_last = reinterpret_cast<int*>(smem + scratch_offset + SCRATCH_BYTES);
-            arrive_and_combine<BM, BN, T::THREADS, CPS>(g, tc, tid, s_last);
-        }
+        // EPI_STORE: the final product, or slice tc.z's subtree root in its
+        // own plane (out_z_stride)
+        store_tile_via_lds<T, STAGES>(acc, g, g.Y + (size_t)tc.z * g.out_z_stride, g.ldy, row0,
+                                      col0, wm, wn, lane, tid, smem);
     }
 }
 
@@ -593,8 +578,7 @@ hipError_t launch_st(const GemmArgs& g, hipStream_t s)
     constexpr bool PK = Stages<T, CPS>::park;
     auto fn = lds_gemm_kernel<T, ST, CPS, EPI, PK, WT>;
     // + the last-arriver flag of a combine (never with 8 chunks per slice)
-    constexpr int bytes = ST * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) + SCRATCH_BYTES +
-                          (EPI == EPI_COMBINE ? 16 : 0);
+    constexpr int bytes = ST * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0);
     static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
     static std::atomic<unsigned long long> lds_set{0};
     const hipError_t attr = ensure_lds_limit(lds_set, reinterpret_cast<const void*>(fn), bytes);
@@ -620,8 +604,7 @@ hipError_t launch(const GemmArgs& g, hipStream_t s)
         // cost no occupancy.
         static const int per_cu = [] {
             constexpr bool PK = St::park;
-            constexpr int bytes = St::shallow * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0) +
-                                  SCRATCH_BYTES + (EPI == EPI_COMBINE ? 16 : 0);
+            constexpr int bytes = St::shallow * T::STAGE_BYTES + (PK ? T::PARK_BYTES : 0);
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                     &n, lds_gemm_kernel<T, St::shallow, CPS, EPI, PK, WT>, T::THREADS, bytes) !=
@@ -644,11 +627,7 @@ hipError_t launch_cps(const GemmArgs& g, int cps, hipStream_t s)
     case 1: return launch<T1, 1, EPI, WT>(g, s);
     case 2: return launch<T, 2, EPI, WT>(g, s);
     case 4: return launch<T, 4, EPI, WT>(g, s);
-    case 8:
-        if constexpr (EPI == EPI_COMBINE)
-            return hipErrorInvalidValue;
-        else
-            return launch<T, 8, EPI, WT>(g, s);
+    case 8: return launch<T, 8, EPI, WT>(g, s);
     }
     return hipErrorInvalidValue;
 }
@@ -701,7 +680,6 @@ hipError_t launch_lds_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStr
 {
     switch (epi) {
     case EPI_STORE: return lds::launch_layout<EPI_STORE>(tile, g, cps, s);
-    case EPI_COMBINE: return lds::launch_layout<EPI_COMBINE>(tile, g, cps, s);
     case EPI_ATOMIC: return lds::launch_layout<EPI_ATOMIC>(tile, g, cps, s);
     }
     return hipErrorInvalidValue;

@@ -72,9 +72,10 @@ bool lds_engine_supports(int tile, const GemmArgs& g, int cps);
 hipError_t launch_lds_gemm(int tile, int epi, const GemmArgs& g, int cps, hipStream_t s);
 hipError_t launch_tree_combine(const float* parts, size_t stride, int count, float* Y, size_t n,
                                hipStream_t s);
-// The same for [M][N] planes into Y rows ldy apart (ldy >= N, N % 4 == 0).
-hipError_t launch_tree_combine_rows(const float* parts, size_t stride, int count, int N, float* Y,
-                                    long ldy, int M, hipStream_t s);
+// The same for [M][N] planes (g.M, g.N) into g.Y at row stride g.ldy, with
+// the addmm epilogue of g when g.epi (N % 4 == 0).
+hipError_t launch_tree_combine_rows(const float* parts, size_t stride, int count,
+                                    const GemmArgs& g, hipStream_t s);
 hipError_t launch_fill_zero(float* Y, long ld, int M, int N, hipStream_t s);
 hipError_t launch_cast_bf16(const float* x, uint16_t* y, size_t n, hipStream_t s);
 
