@@ -107,10 +107,12 @@ int detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
  * result never depend on it (nor on M).  Outputs of at most 64 columns use
  * one slice per chunk (S = P).  For wider ones, with t = the number of
  * 128 x 128 output tiles and Kc = K / P:
- *   t <= 128:       the largest S (<= P) with t*S <= 256, but 4 instead of
+ *   Kc >= 1536, M >= 256 and t >= 96: S = 8;
+ *   else t <= 128:  the largest S (<= P) with t*S <= 256, but 4 instead of
  *                   2 for products of at most 16 rows;
  *   129 <= t < 192: S = 4 if Kc >= 1024, else 1;
- *   t >= 192:       S = 1, but 4 for 257 <= t <= 447 when Kc >= 1024.
+ *   t >= 192:       S = 1, but for 257 <= t <= 447 S = 4 if Kc >= 1024,
+ *                   else 2.
  * Returns 0 for invalid arguments.
  */
 int detred_auto_split(int M, int N, int K);

@@ -169,22 +169,22 @@ void narrow_for_decode(Policy& p, GemmArgs& g, int cps)
 
 // The split for split_k = 0.  The split only decides how many workgroups
 // share the chunk tree, never the bits.  Narrow outputs keep the policy's
-// split (one slice per chunk).  A wide product is sized against the 256 CUs
-// and the LDS engine's stage depth (four stages for a grid of at most 256
-// workgroups, two above):
-//  - fewer than 129 output tiles: the most slices that keep the grid at
-//    or under 256 workgroups (so four stages), except that products of at
-//    most 16 rows take 4 slices rather than 2;
-//  - 129..191 tiles: unsplit when chunks are short (below 1024), else 4
-//    slices;
-//  - 192 or more: unsplit, except 4 slices for 257..447 tiles with chunks
-//    of 1024 or more (an unsplit grid of 1.0-1.75 waves of workgroups
-//    leaves CUs idle through a long K).
+// split (one slice per chunk).  A wide product is sized against the 256 CUs,
+// the LDS engine's stage depth (four stages for a grid of at most 256
+// workgroups) and the cost of its slice roots, which a second launch
+// combines (t = output tiles of 128 x 128, Kc = chunk width):
+//  - Kc >= 1536 with at least 256 rows and t >= 96: 8 slices (one chunk
+//    each, on the 256x256 root tile: the long chunks amortise its
+//    prologue and epilogue);
+//  - t <= 128: the most slices that keep the grid at or under 256
+//    workgroups, except 4 rather than 2 for products of at most 16 rows;
+//  - 129 <= t < 192: 4 slices for Kc >= 1024, else unsplit;
+//  - t >= 192: unsplit, except for 257..447 tiles (1.0-1.75 waves of
+//    workgroups unsplit): 4 slices for Kc >= 1024, 2 for shorter chunks.
 // Measured on MI355X with the weights coming from HBM over M in 1..2560,
-// N in {1024..14336}, K in {4096, 8192, 14336}: e.g. 128x14336x4096 45.2 ->
-// 38.2 us (2 slices, not 4), 768x1024x4096 33.5 -> 29.2 us (4, not 8),
-// 384x14336x8192 171 -> 149 us (4, not 1), 640x4096x4096 56 -> 53 us (1,
-// not 4).
+// N in 1024..14336, K in {4096, 8192, 14336}, S in {1, 2, 4, 8}; e.g.
+// 128x14336x4096 45.2 -> 38.2 us (2 slices, not 4), 768x1024x4096 33.5 ->
+// 29.2 us (4, not 8), 384x8192x14336 at 8 slices 27 % faster than unsplit.
 int auto_split(const Policy& p, int M, int N)
 {
     if (p.tile != TILE_L128)
@@ -192,9 +192,11 @@ int auto_split(const Policy& p, int M, int N)
     const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     const bool long_chunks = p.Kc >= 1024;
     int S = 1;
-    if (tiles >= 192) {
-        if (long_chunks && tiles > 256 && tiles < 448)
-            S = 4;
+    if (p.Kc >= 1536 && M >= 256 && tiles >= 96) {
+        S = 8;
+    } else if (tiles >= 192) {
+        if (tiles > 256 && tiles < 448)
+            S = long_chunks ? 4 : 2;
     } else if (tiles > 128) {
         S = long_chunks ? 4 : 1;
     } else {

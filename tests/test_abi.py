@@ -70,7 +70,9 @@ def test_auto_split():
     assert detred.auto_split(640, 4096, 4096) == 1       # 160 tiles, chunks of 512
     assert detred.auto_split(640, 4096, 8192) == 4       # 160 tiles, chunks of 1024
     assert detred.auto_split(384, 14336, 8192) == 4      # 336 tiles, chunks of 1024
-    assert detred.auto_split(384, 14336, 4096) == 1      # 336 tiles, chunks of 512
+    assert detred.auto_split(384, 14336, 4096) == 2      # 336 tiles, chunks of 512
+    assert detred.auto_split(384, 8192, 14336) == 8      # chunks of 1792, 256+ rows
+    assert detred.auto_split(128, 14336, 14336) == 2     # chunks of 1792, 128 rows
     assert detred.auto_split(512, 14336, 8192) == 1      # 448 tiles
     assert detred.auto_split(1024, 4096, 4096) == 1      # 256 tiles
     assert detred.auto_split(1, 4096, 64) == 1           # one chunk
