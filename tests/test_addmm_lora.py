@@ -223,3 +223,21 @@ def test_lora_forward_batch_invariance(dev):
                                 detred.lora_workspace(m, N, K, r, dev))
         torch.cuda.synchronize()
         np.testing.assert_array_equal(u16(part), u16(full)[:m])
+
+
+@pytest.mark.parametrize("S", [2, 4, 8])
+def test_addmm_bf16_into_padded_rows_every_split(S, dev):
+    """bf16 output into rows ldy > N apart with a bias, on the wide tile (the
+    split's roots combined by the second launch, which applies the
+    epilogue): the same bits as S = 1, nothing written past the rows."""
+    M, N, K = 300, 1032, 4096
+    X, W = inputs.dense_inputs(M, K, N, seed=S)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    bias = dev_f32(inputs.bias_inputs(N, seed=4), dev)
+    ref = addmm(Xd, Wd, bias, 0.75, 1.0, 1, dev, out=torch.int16)
+    Ybig = torch.full((M, N + 24), 77, dtype=torch.int16, device=dev)
+    Y = Ybig[:, 8:8 + N]
+    detred.det_splitk_addmm(Xd, Wd, Y, bias, 0.75, 1.0, S, detred.workspace(M, N, K, S, dev))
+    torch.cuda.synchronize()
+    assert torch.equal(Y, ref), "bf16 addmm into padded rows, S=%d" % S
+    assert torch.all(Ybig[:, :8] == 77) and torch.all(Ybig[:, 8 + N:] == 77)
