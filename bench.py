@@ -358,8 +358,9 @@ def divergence(dev, stream):
 def extensions(dev, stream):
     """The next-row operations, timed alone (median/p10/p90 of 50 launches):
     the one-call LoRA layer (hidden 4096, rank 64, batch 256), addmm with a
-    bias row into a bf16 output on the dense shape, decode attention with
-    the fixed 256-position KV split, and bf16 RMSNorm."""
+    bias row into a bf16 output on the dense shape, the dense product with
+    its weight in the linear-layer layout, decode attention with the fixed
+    256-position KV split, and bf16 RMSNorm."""
     out = {}
     gb = 2
 
@@ -393,6 +394,16 @@ def extensions(dev, stream):
            detred.prepare(detred.det_splitk_addmm, Xdd, Wdd, Yb, bias, 1.0, 1.0, 0,
                           detred.workspace(B, F, H, 0, dev)),
            2 * B * H * F, B * H * gb + H * F * gb + F * 4 + B * F * gb)
+    # the dense product with its weight stored as a linear layer keeps it
+    # ([out, in] = [14336, 4096], K contiguous; the same values): the
+    # transposed-weight kernels read both operands with ds_read_b128
+    Wtd = Wdd.t().contiguous()
+    Yd = torch.empty((B, F), dtype=torch.float32, device=dev)
+    record("dense_linear_weight_%dx%dx%d" % (B, F, H),
+           detred.prepare(detred.det_splitk_gemm, Xdd, Wtd.t(), Yd, 0,
+                          detred.workspace(B, F, H, 0, dev)),
+           2 * B * H * F, B * H * gb + H * F * gb + B * F * 4)
+    del Wtd
     # decode attention: 8B-class GQA (32 query heads, 8 KV heads, head dim
     # 128), 64 sequences of 4096 cached positions; the 1 GiB cache is drawn
     # on the device from a seeded generator
