@@ -358,9 +358,10 @@ def divergence(dev, stream):
 def extensions(dev, stream):
     """The next-row operations, timed alone (median/p10/p90 of 50 launches):
     the one-call LoRA layer (hidden 4096, rank 64, batch 256), addmm with a
-    bias row into a bf16 output on the dense shape, the dense product with
-    its weight in the linear-layer layout, decode attention with the fixed
-    256-position KV split, and bf16 RMSNorm."""
+    bias row into a bf16 output on the dense shape, the dense product and
+    the tree-TP shard roots with their weights in the linear-layer layout,
+    decode attention with the fixed 256-position KV split, and bf16
+    RMSNorm."""
     out = {}
     gb = 2
 
@@ -404,6 +405,15 @@ def extensions(dev, stream):
                           detred.workspace(B, F, H, 0, dev)),
            2 * B * H * F, B * H * gb + H * F * gb + B * F * 4)
     del Wtd
+    # the shard roots of the tree-TP product with the weight of a
+    # row-parallel linear layer ([8192, 8192] = [out, in], K contiguous)
+    Xt, Wt = inputs.dense_inputs(TP_M, TP_K, TP_N, 0)
+    Xtd, Wtt = d16(Xt, dev), d16(Wt, dev).t().contiguous()
+    Pt = torch.empty((TP_T, TP_M, TP_N), dtype=torch.float32, device=dev)
+    record("tp_shards_linear_weight_%dx%dx%d_t%d" % (TP_M, TP_N, TP_K, TP_T),
+           detred.prepare(detred.tree_tp_shards_gemm, Xtd, Wtt.t(), Pt, TP_T),
+           2 * TP_M * TP_K * TP_N, TP_M * TP_K * gb + TP_K * TP_N * gb + TP_M * TP_N * 4)
+    del Wtt, Pt
     # decode attention: 8B-class GQA (32 query heads, 8 KV heads, head dim
     # 128), 64 sequences of 4096 cached positions; the 1 GiB cache is drawn
     # on the device from a seeded generator

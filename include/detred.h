@@ -281,6 +281,24 @@ int tree_tp_shard_gemm(const uint16_t *Xt, int ldx, const uint16_t *Wt,
                        int tp_shards, detred_stream s);
 
 /*
+ * The three tree-TP calls with the weight given transposed, as a
+ * row-parallel linear layer keeps its shard ([out, in] = [N, K], or [N, Kt]
+ * for one rank), K contiguous, rows ldwt elements apart (ldwt >= K, resp.
+ * Kt; ldwt % 8 == 0; 16-byte aligned).  Element (k, n) of the product's
+ * right operand is Wt[n*ldwt + k].  Shards, tree, workspace, errors and
+ * asynchrony as in the untransposed calls, and the same output bits.
+ */
+int tree_tp_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt,
+                    float *Y, int ldy, int M, int N, int K, int tp_shards,
+                    void *ws, size_t ws_bytes, detred_stream s);
+int tree_tp_shards_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt,
+                           int ldwt, float *P, int M, int N, int K,
+                           int tp_shards, detred_stream s);
+int tree_tp_shard_gemm_wt(const uint16_t *Xt, int ldx, const uint16_t *Wtt,
+                          int ldwt, float *Pt, int ldp, int M, int N, int Kt,
+                          int tp_shards, detred_stream s);
+
+/*
  * The fixed binary tree over `count` fp32 arrays of n elements each
  * (count in {1,2,4,8}): parts + i*part_stride (elements) is array i;
  * Y[e] = ((p0+p1)+(p2+p3))+... as in the canonical tree's top levels.

@@ -540,10 +540,15 @@ int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, f
     return hip_status(launch_slice_gemm(pa.tile, EPI_ATOMIC, g, p.P / S, hs));
 }
 
-int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
-                 int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes, detred_stream s)
+}  // extern "C"
+
+namespace {
+
+int tree_tp_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* Y,
+                 int ldy, int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes,
+                 detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     Policy p = plan(M, N, K);
@@ -554,6 +559,7 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     if (K == 0)
         return hip_status(launch_fill_zero(Y, ldy, M, N, hs));
     GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, T);
+    g.wt = wt;
     if (T == 1) {
         narrow_for_decode(p, g, p.P);
         return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
@@ -565,10 +571,10 @@ int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* 
     return run_roots_then_combine(p, g, T, (float*)ws, hs);
 }
 
-int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* P, int M,
-                        int N, int K, int tp_shards, detred_stream s)
+int tree_tp_shards_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* P,
+                        int M, int N, int K, int tp_shards, detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, P, N, M, N, K);
+    int st = check_gemm(X, ldx, W, ldw, P, N, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     Policy p = plan(M, N, K);
@@ -580,14 +586,15 @@ int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, 
         return hip_status(e);
     }
     GemmArgs g = make_args(p, X, ldx, W, ldw, P, N, M, N, K, tp_shards);
+    g.wt = wt;
     g.out_z_stride = (long)M * N;
     widen_for_roots(p, g, p.P / tp_shards);
     narrow_for_decode(p, g, p.P / tp_shards);
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
 }
 
-int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, float* Pt,
-                       int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+int tree_tp_shard_impl(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, bool wt,
+                       float* Pt, int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
 {
     if (!pow2_le8(tp_shards) || Kt < 0)
         return DETRED_EINVAL;
@@ -595,7 +602,7 @@ int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
     if (Kl > 0x7fffffffL)
         return DETRED_EINVAL;
     const int K = (int)Kl;
-    int st = check_gemm(Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt);
+    int st = check_gemm(Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     Policy p = plan(M, N, K);
@@ -606,9 +613,51 @@ int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
         return hip_status(launch_fill_zero(Pt, ldp, M, N, hs));
     // the shard's own K range is chunks [0, P/T) of width K/P
     GemmArgs g = make_args(p, Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, 1);
+    g.wt = wt;
     widen_for_roots(p, g, p.P / tp_shards);
     narrow_for_decode(p, g, p.P / tp_shards);
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
+                 int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes, detred_stream s)
+{
+    return tree_tp_impl(X, ldx, W, ldw, false, Y, ldy, M, N, K, tp_shards, ws, ws_bytes, s);
+}
+
+int tree_tp_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* Y, int ldy,
+                    int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes,
+                    detred_stream s)
+{
+    return tree_tp_impl(X, ldx, Wt, ldwt, true, Y, ldy, M, N, K, tp_shards, ws, ws_bytes, s);
+}
+
+int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* P, int M,
+                        int N, int K, int tp_shards, detred_stream s)
+{
+    return tree_tp_shards_impl(X, ldx, W, ldw, false, P, M, N, K, tp_shards, s);
+}
+
+int tree_tp_shards_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* P,
+                           int M, int N, int K, int tp_shards, detred_stream s)
+{
+    return tree_tp_shards_impl(X, ldx, Wt, ldwt, true, P, M, N, K, tp_shards, s);
+}
+
+int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, float* Pt,
+                       int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+{
+    return tree_tp_shard_impl(Xt, ldx, Wt, ldw, false, Pt, ldp, M, N, Kt, tp_shards, s);
+}
+
+int tree_tp_shard_gemm_wt(const uint16_t* Xt, int ldx, const uint16_t* Wtt, int ldwt, float* Pt,
+                          int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+{
+    return tree_tp_shard_impl(Xt, ldx, Wtt, ldwt, true, Pt, ldp, M, N, Kt, tp_shards, s);
 }
 
 int tree_combine_f32(const float* parts, size_t part_stride, int count, float* Y, size_t n,

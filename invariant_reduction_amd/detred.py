@@ -47,6 +47,9 @@ SIGNATURES = {
     "tree_tp_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "tree_tp_shards_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _P], _I),
     "tree_tp_shard_gemm": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
+    "tree_tp_gemm_wt": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "tree_tp_shards_gemm_wt": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _P], _I),
+    "tree_tp_shard_gemm_wt": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "tree_combine_f32": ([_P, _Z, _I, _P, _Z, _P], _I),
     "detred_f32_to_bf16": ([_P, _P, _Z, _P], _I),
     "inv_rmsnorm": ([_P, _P, _P, _I, _I, _F, _P], _I),
@@ -304,40 +307,44 @@ def atomic_splitk_gemm(X, W, Y, split_k=0, stream=None):
 
 @_entry
 def tree_tp_gemm(X, W, Y, tp_shards, ws=None, stream=None):
-    """Tree-based TP-invariant product over tp_shards virtual shards."""
+    """Tree-based TP-invariant product over tp_shards virtual shards.  W
+    may be the transpose view of a row-major [N, K] weight (tree_tp_gemm_wt;
+    same bits)."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
-    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    pw, ldw, wt = _weight(W)
     py, ldy = _mat(Y, (torch.float32,), "Y")
     M, N, K = _gemm_dims(X, W, Y)
     pws, nws = _ws(ws)
-    return "tree_tp_gemm", (px, ldx, pw, ldw, py, ldy, M, N, K, tp_shards, pws, nws,
-                              _stream(stream))
+    return ("tree_tp_gemm_wt" if wt else "tree_tp_gemm"), (
+        px, ldx, pw, ldw, py, ldy, M, N, K, tp_shards, pws, nws, _stream(stream))
 
 
 @_entry
 def tree_tp_shards_gemm(X, W, P, tp_shards, stream=None):
     """Phase 1 of tree_tp_gemm: P[t] (fp32 [T, M, N], contiguous) = shard
-    t's subtree root, all shards in one launch."""
+    t's subtree root, all shards in one launch.  W may be a transposed
+    [N, K] weight's view (tree_tp_shards_gemm_wt)."""
     px, ldx = _mat(X, _BF16_TYPES, "X")
-    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    pw, ldw, wt = _weight(W)
     M, K = X.shape
     K2, N = W.shape
     if K2 != K or tuple(P.shape) != (tp_shards, M, N) or P.dtype != torch.float32 \
             or not P.is_cuda or not P.is_contiguous():
         raise ValueError("P must be a contiguous fp32 GPU tensor of shape (T, M, N)")
-    return "tree_tp_shards_gemm", (px, ldx, pw, ldw, ctypes.c_void_p(P.data_ptr()), M, N, K,
-                                   tp_shards, _stream(stream))
+    return ("tree_tp_shards_gemm_wt" if wt else "tree_tp_shards_gemm"), (
+        px, ldx, pw, ldw, ctypes.c_void_p(P.data_ptr()), M, N, K, tp_shards, _stream(stream))
 
 
 @_entry
 def tree_tp_shard_gemm(Xt, Wt, Pt, tp_shards, stream=None):
-    """One rank's shard of tree_tp_gemm: Pt = subtree root of Xt Wt."""
+    """One rank's shard of tree_tp_gemm: Pt = subtree root of Xt Wt (Wt
+    [Kt, N], or the transpose view of the rank's [N, Kt] weight shard)."""
     px, ldx = _mat(Xt, _BF16_TYPES, "Xt")
-    pw, ldw = _mat(Wt, _BF16_TYPES, "Wt")
+    pw, ldw, wt = _weight(Wt)
     pp, ldp = _mat(Pt, (torch.float32,), "Pt")
     M, N, Kt = _gemm_dims(Xt, Wt, Pt)
-    return "tree_tp_shard_gemm", (px, ldx, pw, ldw, pp, ldp, M, N, Kt, tp_shards,
-                                    _stream(stream))
+    return ("tree_tp_shard_gemm_wt" if wt else "tree_tp_shard_gemm"), (
+        px, ldx, pw, ldw, pp, ldp, M, N, Kt, tp_shards, _stream(stream))
 
 
 @_entry

@@ -143,6 +143,19 @@ def test_transposed_weight_entry_points_reject():
     a = g(X=None, W=None)
     a[6] = 0                                                      # M == 0
     assert L.det_splitk_gemm_wt(*a) == detred.OK
+    # tree_tp_gemm_wt(X, ldx, Wt, ldwt, Y, ldy, M, N, K, T, ws, ws_bytes, s)
+    assert L.tree_tp_gemm_wt(*g(ldw=16)) == detred.EINVAL          # ldwt < K
+    assert L.tree_tp_gemm_wt(*g(ldw=516)) == detred.EINVAL         # ldwt % 8 != 0
+    assert L.tree_tp_gemm_wt(*g(S=3)) == detred.EUNSUPPORTED
+    assert L.tree_tp_gemm_wt(*g(S=8)) == detred.EWORKSPACE
+    # tree_tp_shards_gemm_wt(X, ldx, Wt, ldwt, P, M, N, K, T, s)
+    assert L.tree_tp_shards_gemm_wt(A16, 512, A16b, 16, A16c, 16, 16, 512, 8, None) == detred.EINVAL
+    assert L.tree_tp_shards_gemm_wt(A16, 512, A16b, 512, A16c, 16, 16, 512, 3, None) == \
+        detred.EUNSUPPORTED
+    # tree_tp_shard_gemm_wt(Xt, ldx, Wt, ldwt, Pt, ldp, M, N, Kt, T, s): ldwt >= Kt
+    assert L.tree_tp_shard_gemm_wt(A16, 64, A16b, 32, A16c, 16, 16, 16, 64, 8, None) == detred.EINVAL
+    assert L.tree_tp_shard_gemm_wt(A16, 64, A16b, 64, A16c, 16, 16, 16, 64, 3, None) == \
+        detred.EINVAL
     # det_splitk_addmm_wt(X, ldx, Wt, ldwt, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K, S, ws, ws_bytes, s)
     am = lambda **kw: [A16, 512, A16b, kw.get("ldw", 512), A16c, kw.get("ldc", 16), f(1.0), f(1.0),
                        A16, 16, kw.get("dt", detred.F32), 16, 16, 512, 1, None, 0, None]

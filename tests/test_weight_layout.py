@@ -92,3 +92,36 @@ def test_dense_workload_full_size(dev):
     torch.cuda.synchronize()
     assert_bitwise(got, ref, "dense workload, Wt vs W")
     assert_gemm_parity(got, X, W, rows=[0, 1, 127, 128, 255])
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 2048), (520, 3080, 8192), (5, 1032, 8192)])
+def test_tree_tp_transposed_weight(M, N, K, dev):
+    """tree_tp_gemm, tree_tp_shards_gemm and tree_tp_shard_gemm with the
+    weight as a row-parallel linear layer keeps it ([N, K]; per rank the
+    [N, K/T] columns of it): the bits of the row-major calls for every T,
+    on the 128x128 and 256x256 root tiles and the decode tile."""
+    X, W = inputs.dense_inputs(M, K, N, seed=M + 7)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    Wtv = transposed(W, dev)
+    ref = det(Xd, Wd, 1, dev)
+    for T in (1, 2, 4, 8):
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        detred.tree_tp_gemm(Xd, Wtv, Y, T, detred.workspace(M, N, K, T, dev))
+        P = torch.empty((T, M, N), dtype=torch.float32, device=dev)
+        detred.tree_tp_shards_gemm(Xd, Wtv, P, T)
+        Yp = torch.empty_like(Y)
+        detred.tree_combine_f32(P, Yp)
+        Kt = K // T
+        parts = torch.empty((T, M, N), dtype=torch.float32, device=dev)
+        Wt_rows = Wtv.t()  # [N, K], K contiguous
+        for t in range(T):
+            Xs = Xd[:, t * Kt:(t + 1) * Kt].contiguous()
+            Ws = Wt_rows[:, t * Kt:(t + 1) * Kt].contiguous()  # the rank's [N, Kt] shard
+            detred.tree_tp_shard_gemm(Xs, Ws.t(), parts[t], T)
+        Yc = torch.empty_like(Y)
+        detred.tree_combine_f32(parts, Yc)
+        torch.cuda.synchronize()
+        assert_bitwise(Y, ref, "tree_tp_gemm with [N,K] weight, T=%d" % T)
+        assert_bitwise(Yp, ref, "tree_tp_shards_gemm with [N,K] weight + combine, T=%d" % T)
+        assert_bitwise(Yc, ref, "rank shards with [N,Kt] weights + combine, T=%d" % T)
+    assert_gemm_parity(ref, X, W, rows=[0, M - 1])
