@@ -222,8 +222,9 @@ size_t det_lora_workspace_bytes(int M, int N, int K, int r);
  * i.e. Y = bf16(base + scale*(zb*B)).  X [M,K] ld ldx, W [K,N] ld ldw,
  * A [K,r] ld lda, B [r,N] ld ldb, all bf16; Y bf16 ld ldy.  r % 8 == 0,
  * K % 8 == 0, N % 8 == 0.  ws: det_lora_workspace_bytes(M,N,K,r) bytes,
- * 256-byte aligned, zeroed once with detred_workspace_init.  Three launches
- * on s.  The bits of Y do not depend on M.
+ * 256-byte aligned, zeroed once with detred_workspace_init.  Three to five
+ * launches on s (a split base product or shrink adds its combine launch).
+ * The bits of Y do not depend on M.
  */
 int det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
                      const uint16_t *A, int lda, const uint16_t *B, int ldb,
