@@ -287,3 +287,36 @@ def test_torch_mode_registers_and_restores():
         assert torch_ops.is_enabled()
         assert torch.equal(torch.mm(a, a.t()), torch.full((4, 4), 8.0, dtype=torch.bfloat16))
     assert not torch_ops.is_enabled()
+
+
+def _documented_split(M, N, K):
+    """The automatic split as include/detred.h states it, written out here
+    independently of the library."""
+    P = 8 if (K >= 256 and K % 256 == 0) else 1
+    if N <= 64 or P == 1:
+        return None  # narrow outputs and one-chunk K keep the policy's split
+    Kc = K // P
+    t = ((M + 127) // 128) * ((N + 127) // 128)
+    if Kc >= 1536 and M >= 256 and t >= 96:
+        S = 8
+    elif t <= 128:
+        S = 1
+        while S < P and t * S * 2 <= 256:
+            S *= 2
+        if S == 2 and M <= 16:
+            S = 4
+    elif t < 192:
+        S = 4 if Kc >= 1024 else 1
+    else:
+        S = (4 if Kc >= 1024 else 2) if 257 <= t <= 447 else 1
+    return min(S, P)
+
+
+def test_auto_split_follows_the_documented_rule():
+    for K in (256, 1024, 4096, 8192, 12288, 14336, 16384):
+        for N in (72, 128, 1000, 1024, 4096, 8192, 14336, 28672):
+            for M in (1, 2, 16, 17, 63, 64, 65, 128, 192, 255, 256, 257, 384, 512, 640, 768, 1024,
+                      1536, 2048, 2560, 3000, 4096, 8192):
+                want = _documented_split(M, N, K)
+                if want is not None:
+                    assert detred.auto_split(M, N, K) == want, (M, N, K)
