@@ -236,7 +236,7 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[T::FM][T::FN], const bf16x
 // Subtree roots (several planes, out_z_stride set) go out with plain
 // stores, as the combine reads them next; final outputs non-temporally (a
 // large output would push out the operands still being read).
-template <class T, int STAGES>
+template <class T, int STAGES, bool EPI_OK = true>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::FN],
                                                    const GemmArgs& g, float* out, int ld, int row0,
                                                    int col0, int wm, int wn, int lane, int tid,
@@ -287,7 +287,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::
                 const int r = v / (BN / 4), c4 = v % (BN / 4);
                 val[i] = *reinterpret_cast<const u32x4*>(t + r * BN + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
             }
-            if (!g.epi) {
+            if (!EPI_OK || !g.epi) {
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     out + (size_t)prow0 * ld + col0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
                 auto put = [&](auto policy) {
@@ -307,6 +307,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::
                     put(std::integral_constant<int, CPOL_NT>());
                 continue;
             }
+            if constexpr (EPI_OK) {
             // the final product of a single-slice addmm: y = beta*C + alpha*p
             __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<float*>(g.C ? g.C : g.Y) + (size_t)prow0 * g.ldc + col0, 0,
@@ -349,8 +350,40 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[T::FM][T::
                         o, ry, in ? (int)((r * g.ldy + 4 * c4) * 4) : OOB, 0, CPOL_NT);
                 }
             }
+            }
         }
     }
+}
+
+// Roots of the 256x256 tile straight from the MFMA layout: a lane holds four
+// rows of one column per 16x16 block, so each store is 4 bytes and one
+// instruction writes four 64-byte row pieces.  No LDS pass and no barrier:
+// a wave stores as soon as its K loop ends.  Plain stores (the combine
+// reads the roots next); pieces outside M x N are dropped by the buffer's
+// range check.
+template <class T>
+__device__ __forceinline__ void store_roots_direct(const f32x4 (&acc)[T::FM][T::FN], float* out,
+                                                   int ld, int M, int N, int wrow0, int wcol0,
+                                                   int lane)
+{
+    constexpr int OOB = (int)0x80000000u;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        out + (size_t)wrow0 * ld + wcol0, 0, 0x7fffffff, RAW_BUFFER_FLAGS);
+    // the lane index made opaque here, so that the 128 store offsets are
+    // computed where they are used rather than hoisted into the K loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = fm * 16 + 4 * (l >> 4) + q, c = fn * 16 + (l & 15);
+                const bool in = (wrow0 + r < M) && (wcol0 + c < N);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[fm][fn][q]), rs,
+                                                      in ? (r * ld + c) * 4 : OOB, 0, 0);
+            }
 }
 
 template <class T, int STAGES, int CPS, int EPI, bool PARK, bool WT>
@@ -547,8 +580,22 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
     } else {
         // EPI_STORE: the final product, or slice tc.z's subtree root in its
         // own plane (out_z_stride)
-        store_tile_via_lds<T, STAGES>(acc, g, g.Y + (size_t)tc.z * g.out_z_stride, g.ldy, row0,
-                                      col0, wm, wn, lane, tid, smem);
+        float* out = g.Y + (size_t)tc.z * g.out_z_stride;
+        if constexpr (T::BM == 256) {
+            // the root tile: plain roots only, never an addmm epilogue (the
+            // direct form only with a row-major W: beside the transposed
+            // operand's addressing it would not fit the registers)
+            if constexpr (!WT) {
+                if (g.direct_roots) {
+                    store_roots_direct<T>(acc, out, g.ldy, g.M, g.N, wrow0, wcol0, lane);
+                    return;
+                }
+            }
+            store_tile_via_lds<T, STAGES, false>(acc, g, out, g.ldy, row0, col0, wm, wn, lane,
+                                                 tid, smem);
+        } else {
+            store_tile_via_lds<T, STAGES>(acc, g, out, g.ldy, row0, col0, wm, wn, lane, tid, smem);
+        }
     }
 }
 

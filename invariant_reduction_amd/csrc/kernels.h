@@ -58,6 +58,9 @@ struct GemmArgs {
     long ldc;             // 0: C is one row, broadcast to every row
     float alpha, beta;
     int out_bf16;
+    // 256x256 root tile only: store the roots straight from the MFMA
+    // registers (4-byte stores) instead of through LDS
+    int direct_roots;
 };
 
 void tile_shape(int tile, int* bm, int* bn);
