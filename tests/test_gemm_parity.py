@@ -218,3 +218,21 @@ def test_cast_matches_oracle(dev):
     detred.detred_f32_to_bf16(dev_f32(x, dev), y)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(y).view(np.uint16), oracle.f32_to_bf16(x))
+
+
+def test_rank_shard_on_root_tile_into_padded_rows(dev):
+    """One rank's shard large enough for the 256x256 root tile (2048 x 8192
+    output, one chunk of 1024 per shard at T = 8), its root stored straight
+    from the registers into rows ldp > N apart: the bits of the contiguous
+    call, nothing written past the rows."""
+    M, N, Kt, T = 2048, 8192, 1024, 8
+    X, W = inputs.dense_inputs(M, Kt, N, seed=17)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    ref = torch.empty((M, N), dtype=torch.float32, device=dev)
+    detred.tree_tp_shard_gemm(Xd, Wd, ref, T)
+    Pbig = torch.full((M, N + 8), -3.0, dtype=torch.float32, device=dev)
+    detred.tree_tp_shard_gemm(Xd, Wd, Pbig[:, :N], T)
+    torch.cuda.synchronize()
+    assert_bitwise(Pbig[:, :N], ref, "shard root into padded rows")
+    assert torch.all(Pbig[:, N:] == -3.0), "wrote past the row"
+    assert_gemm_parity(ref, X, W, rows=[0, 1023, 2047])
