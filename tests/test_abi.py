@@ -320,3 +320,23 @@ def test_auto_split_follows_the_documented_rule():
                 want = _documented_split(M, N, K)
                 if want is not None:
                     assert detred.auto_split(M, N, K) == want, (M, N, K)
+
+
+def test_workspace_sizes_cover_the_partial_planes():
+    """For every split the library may pick, detred_gemm_workspace_bytes
+    covers S fp32 [M][N] planes (the slice roots) plus one counter per
+    output tile, rounded to 256 bytes; S = 1 needs none."""
+    L = detred.lib()
+    for K in (64, 512, 4096, 14336):
+        for N in (8, 16, 64, 72, 1024, 14336):
+            for M in (1, 7, 64, 255, 256, 1000, 4096):
+                for S in (0, 1, 2, 4, 8):
+                    got = L.detred_gemm_workspace_bytes(M, N, K, S)
+                    s = S if S else detred.auto_split(M, N, K)
+                    P = 8 if (K >= 256 and K % 256 == 0) else 1
+                    if s <= 1 or s > P:
+                        if s <= 1:
+                            assert got == 0, (M, N, K, S)
+                        continue
+                    assert got % 256 == 0, (M, N, K, S)
+                    assert got >= s * M * N * 4 + 4, (M, N, K, S)  # planes + at least one counter
