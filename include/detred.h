@@ -82,7 +82,7 @@ typedef void *detred_stream; /* hipStream_t; NULL = null stream */
 enum { DETRED_F32 = 0, DETRED_BF16 = 1 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
-const char *detred_status_string(int status);
+const char *detred_status_string(detred_status status);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int detred_version(void);
@@ -98,8 +98,8 @@ int detred_version(void);
  *                    give every CU an output tile (detred_auto_split).
  * Returns EINVAL for N < 0 or K < 0.
  */
-int detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
-                  int *tile_n, int *default_split);
+detred_status detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m,
+                            int *tile_n, int *default_split);
 
 /*
  * The split that split_k = 0 selects for an M x N x K product.  The split
@@ -122,8 +122,8 @@ int detred_auto_split(int M, int N, int K);
  * (tp_shards = S) needs for an M x N output with reduction length K:
  * S fp32 partial arrays of M*N elements plus one 32-bit counter per output
  * tile, rounded up to 256 bytes.  S = 0 means detred_auto_split(M, N, K).
- * 0 when S == 1 (no workspace is used).  Returns 0 for invalid arguments as
- * well.
+ * 0 when S == 1 (no workspace is used), and 0 for a split the products reject
+ * (S not in {1,2,4,8}, or S > P) and for invalid arguments.
  */
 size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards);
 
@@ -133,7 +133,7 @@ size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards);
  * counters at zero again when it completes.  One workspace serves one call
  * in flight at a time.
  */
-int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
+detred_status detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
 
 /*
  * Deterministic split-K product Y[M,N] (fp32) = X[M,K] W[K,N] (bf16), the
@@ -152,9 +152,10 @@ int detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
  * tile's rows with 32-bit offsets; EUNSUPPORTED otherwise).
  * The bits of Y do not depend on S.
  */
-int det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
-                    float *Y, int ldy, int M, int N, int K, int split_k,
-                    void *ws, size_t ws_bytes, detred_stream s);
+detred_status det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W,
+                              int ldw, float *Y, int ldy, int M, int N, int K,
+                              int split_k, void *ws, size_t ws_bytes,
+                              detred_stream s);
 
 /*
  * Deterministic addmm, the form of torch.addmm that the "Batch Invariant Ops"
@@ -175,10 +176,11 @@ int det_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * det_splitk_gemm; EINVAL for a bad y_dtype, C or ldc.  K == 0 gives
  * y = beta*C + alpha*(+0).  Row i of Y depends only on row i of X (and of C).
  */
-int det_splitk_addmm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
-                     const float *C, int ldc, float alpha, float beta,
-                     void *Y, int ldy, int y_dtype, int M, int N, int K,
-                     int split_k, void *ws, size_t ws_bytes, detred_stream s);
+detred_status det_splitk_addmm(const uint16_t *X, int ldx, const uint16_t *W,
+                               int ldw, const float *C, int ldc, float alpha,
+                               float beta, void *Y, int ldy, int y_dtype, int M,
+                               int N, int K, int split_k, void *ws, size_t ws_bytes,
+                               detred_stream s);
 
 /*
  * det_splitk_gemm and det_splitk_addmm with the weight given transposed:
@@ -192,13 +194,15 @@ int det_splitk_addmm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * bits equal theirs for W = Wt^T; workspace, errors and asynchrony as there
  * (EINVAL also for ldwt < K).
  */
-int det_splitk_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt,
-                       float *Y, int ldy, int M, int N, int K, int split_k,
-                       void *ws, size_t ws_bytes, detred_stream s);
-int det_splitk_addmm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt,
-                        const float *C, int ldc, float alpha, float beta,
-                        void *Y, int ldy, int y_dtype, int M, int N, int K,
-                        int split_k, void *ws, size_t ws_bytes, detred_stream s);
+detred_status det_splitk_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt,
+                                 int ldwt, float *Y, int ldy, int M, int N, int K,
+                                 int split_k, void *ws, size_t ws_bytes,
+                                 detred_stream s);
+detred_status det_splitk_addmm_wt(const uint16_t *X, int ldx, const uint16_t *Wt,
+                                  int ldwt, const float *C, int ldc, float alpha,
+                                  float beta, void *Y, int ldy, int y_dtype, int M,
+                                  int N, int K, int split_k, void *ws,
+                                  size_t ws_bytes, detred_stream s);
 
 /*
  * Workspace of det_lora_forward for an M x N layer output with input width K
@@ -226,10 +230,11 @@ size_t det_lora_workspace_bytes(int M, int N, int K, int r);
  * launches on s (a split base product or shrink adds its combine launch).
  * The bits of Y do not depend on M.
  */
-int det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
-                     const uint16_t *A, int lda, const uint16_t *B, int ldb,
-                     float scale, uint16_t *Y, int ldy, int M, int N, int K,
-                     int r, void *ws, size_t ws_bytes, detred_stream s);
+detred_status det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W,
+                               int ldw, const uint16_t *A, int lda,
+                               const uint16_t *B, int ldb, float scale, uint16_t *Y,
+                               int ldy, int M, int N, int K, int r, void *ws,
+                               size_t ws_bytes, detred_stream s);
 
 /*
  * The nondeterministic control: the same slice products as det_splitk_gemm,
@@ -240,9 +245,9 @@ int det_lora_forward(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * zero fill is part of the call.  Results agree with the oracle to the same
  * tolerance but are not bit-reproducible.
  */
-int atomic_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
-                       float *Y, int ldy, int M, int N, int K, int split_k,
-                       detred_stream s);
+detred_status atomic_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W,
+                                 int ldw, float *Y, int ldy, int M, int N, int K,
+                                 int split_k, detred_stream s);
 
 /*
  * Tree-based TP-invariant product on one GPU (TBIK, arXiv 2511.17826,
@@ -255,9 +260,9 @@ int atomic_splitk_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * ws: T*M*N fp32 shard buffers (detred_gemm_workspace_bytes(M,N,K,T));
  * may be NULL when T == 1.  Y's bits equal det_splitk_gemm's for every T.
  */
-int tree_tp_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
-                 float *Y, int ldy, int M, int N, int K, int tp_shards,
-                 void *ws, size_t ws_bytes, detred_stream s);
+detred_status tree_tp_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
+                           float *Y, int ldy, int M, int N, int K, int tp_shards,
+                           void *ws, size_t ws_bytes, detred_stream s);
 
 /*
  * Phase 1 of tree_tp_gemm on its own: all T shards in one launch, shard t's
@@ -265,9 +270,9 @@ int tree_tp_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * P must hold T*M*N floats, 16-byte aligned.  tree_combine_f32(P, M*N, T,
  * Y, M*N) is phase 2 (the cross-rank reduction) for a contiguous Y.
  */
-int tree_tp_shards_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
-                        float *P, int M, int N, int K, int tp_shards,
-                        detred_stream s);
+detred_status tree_tp_shards_gemm(const uint16_t *X, int ldx, const uint16_t *W,
+                                  int ldw, float *P, int M, int N, int K,
+                                  int tp_shards, detred_stream s);
 
 /*
  * One shard of tree_tp_gemm at its own share shape: what rank t of a
@@ -277,9 +282,9 @@ int tree_tp_shards_gemm(const uint16_t *X, int ldx, const uint16_t *W, int ldw,
  * P/T chunks of width K/8 each.  Requires Kt*T to satisfy the P = 8 rule
  * (Kt*T >= 256, Kt*T % 256 == 0) when T > 1.
  */
-int tree_tp_shard_gemm(const uint16_t *Xt, int ldx, const uint16_t *Wt,
-                       int ldw, float *Pt, int ldp, int M, int N, int Kt,
-                       int tp_shards, detred_stream s);
+detred_status tree_tp_shard_gemm(const uint16_t *Xt, int ldx, const uint16_t *Wt,
+                                 int ldw, float *Pt, int ldp, int M, int N, int Kt,
+                                 int tp_shards, detred_stream s);
 
 /*
  * The three tree-TP calls with the weight given transposed, as a
@@ -289,15 +294,17 @@ int tree_tp_shard_gemm(const uint16_t *Xt, int ldx, const uint16_t *Wt,
  * right operand is Wt[n*ldwt + k].  Shards, tree, workspace, errors and
  * asynchrony as in the untransposed calls, and the same output bits.
  */
-int tree_tp_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt, int ldwt,
-                    float *Y, int ldy, int M, int N, int K, int tp_shards,
-                    void *ws, size_t ws_bytes, detred_stream s);
-int tree_tp_shards_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt,
-                           int ldwt, float *P, int M, int N, int K,
-                           int tp_shards, detred_stream s);
-int tree_tp_shard_gemm_wt(const uint16_t *Xt, int ldx, const uint16_t *Wtt,
-                          int ldwt, float *Pt, int ldp, int M, int N, int Kt,
-                          int tp_shards, detred_stream s);
+detred_status tree_tp_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt,
+                              int ldwt, float *Y, int ldy, int M, int N, int K,
+                              int tp_shards, void *ws, size_t ws_bytes,
+                              detred_stream s);
+detred_status tree_tp_shards_gemm_wt(const uint16_t *X, int ldx, const uint16_t *Wt,
+                                     int ldwt, float *P, int M, int N, int K,
+                                     int tp_shards, detred_stream s);
+detred_status tree_tp_shard_gemm_wt(const uint16_t *Xt, int ldx,
+                                    const uint16_t *Wtt, int ldwt, float *Pt,
+                                    int ldp, int M, int N, int Kt, int tp_shards,
+                                    detred_stream s);
 
 /*
  * The fixed binary tree over `count` fp32 arrays of n elements each
@@ -306,8 +313,8 @@ int tree_tp_shard_gemm_wt(const uint16_t *Xt, int ldx, const uint16_t *Wtt,
  * parts and Y 16-byte aligned, part_stride and n multiples of 4.
  * Y may not overlap the parts.
  */
-int tree_combine_f32(const float *parts, size_t part_stride, int count,
-                     float *Y, size_t n, detred_stream s);
+detred_status tree_combine_f32(const float *parts, size_t part_stride, int count,
+                               float *Y, size_t n, detred_stream s);
 
 /*
  * The explicit binary32 -> bf16 cast (round to nearest, ties to even) that
@@ -315,7 +322,8 @@ int tree_combine_f32(const float *parts, size_t part_stride, int count,
  * (split-K paper, Q&A: shrink, then expand).  n elements; x, y 16-byte
  * aligned, n % 8 == 0.  NaN stays NaN.
  */
-int detred_f32_to_bf16(const float *x, uint16_t *y, size_t n, detred_stream s);
+detred_status detred_f32_to_bf16(const float *x, uint16_t *y, size_t n,
+                                 detred_stream s);
 
 /*
  * Batch-invariant RMSNorm (Thinking Machines article, 2-3 and 3-1: each row
@@ -327,16 +335,17 @@ int detred_f32_to_bf16(const float *x, uint16_t *y, size_t n, detred_stream s);
  * contiguous and 16-byte aligned; hidden % 8 == 0, 0 < hidden <= 65536
  * (EUNSUPPORTED otherwise).  rows == 0 launches nothing.
  */
-int inv_rmsnorm(const uint16_t *x, const uint16_t *gamma, float *y, int rows,
-                int hidden, float eps, detred_stream s);
+detred_status inv_rmsnorm(const uint16_t *x, const uint16_t *gamma, float *y,
+                          int rows, int hidden, float eps, detred_stream s);
 
 /*
  * inv_rmsnorm with a bf16 output: the same binary32 values, each rounded to
  * bf16 (nearest even) as it is stored.  y bf16 [rows][hidden], 16-byte
  * aligned; other arguments and errors as inv_rmsnorm.
  */
-int inv_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, uint16_t *y,
-                     int rows, int hidden, float eps, detred_stream s);
+detred_status inv_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma,
+                               uint16_t *y, int rows, int hidden, float eps,
+                               detred_stream s);
 
 /*
  * Batch-invariant log_softmax over the last dimension (Batch Invariant Ops,
@@ -346,8 +355,8 @@ int inv_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, uint16_t *y,
  * contiguous, 16-byte aligned, cols % 4 == 0 and cols > 0 (EUNSUPPORTED
  * otherwise).  x and y may be the same buffer.
  */
-int inv_log_softmax(const float *x, float *y, int rows, int cols,
-                    detred_stream s);
+detred_status inv_log_softmax(const float *x, float *y, int rows, int cols,
+                              detred_stream s);
 
 /*
  * Batch-invariant mean over the last dimension (Batch Invariant Ops,
@@ -356,7 +365,8 @@ int inv_log_softmax(const float *x, float *y, int rows, int cols,
  * x fp32 [rows][cols] contiguous, 16-byte aligned, cols % 4 == 0, cols > 0;
  * y fp32 [rows].
  */
-int inv_mean(const float *x, float *y, int rows, int cols, detred_stream s);
+detred_status inv_mean(const float *x, float *y, int rows, int cols,
+                       detred_stream s);
 
 /*
  * inv_log_softmax and inv_mean of the same rows in one pass over x: y as
@@ -367,8 +377,8 @@ int inv_mean(const float *x, float *y, int rows, int cols, detred_stream s);
  * 4-byte aligned; other arguments and errors as inv_log_softmax (x and y may
  * be the same buffer).
  */
-int inv_log_softmax_mean(const float *x, float *y, float *mu, int rows, int cols,
-                         detred_stream s);
+detred_status inv_log_softmax_mean(const float *x, float *y, float *mu, int rows,
+                                   int cols, detred_stream s);
 
 /*
  * Workspace of inv_decode_attention: the per-chunk results of B*Hq query
@@ -402,11 +412,12 @@ size_t inv_decode_attention_workspace_bytes(int B, int Hq, int D, int max_len);
  * otherwise).  ws: inv_decode_attention_workspace_bytes(B, Hq, D, max_len)
  * bytes, 256-byte aligned (EWORKSPACE).  Two launches on s.
  */
-int inv_decode_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         long kv_stride_b, long kv_stride_h, long kv_stride_t,
-                         const int *lens, float *out, int B, int Hq, int Hkv, int D,
-                         int max_len, float scale, void *ws, size_t ws_bytes,
-                         detred_stream s);
+detred_status inv_decode_attention(const uint16_t *q, const uint16_t *k,
+                                   const uint16_t *v, long kv_stride_b,
+                                   long kv_stride_h, long kv_stride_t,
+                                   const int *lens, float *out, int B, int Hq,
+                                   int Hkv, int D, int max_len, float scale,
+                                   void *ws, size_t ws_bytes, detred_stream s);
 
 #ifdef __cplusplus
 }

@@ -75,12 +75,12 @@ size_t counter_bytes(const Policy& p, int M, int N)
     return round_up(tm * tn * sizeof(unsigned), 256);
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? DETRED_OK : DETRED_EHIP; }
+detred_status hip_status(hipError_t e) { return e == hipSuccess ? DETRED_OK : DETRED_EHIP; }
 
 // Checks shared by the GEMM entry points (wt: W given transposed, [N][K]
 // with rows ldw apart).
-int check_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* Y, int ldy,
-               int M, int N, int K, bool wt = false)
+detred_status check_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* Y,
+                         int ldy, int M, int N, int K, bool wt = false)
 {
     if (M < 0 || N < 0 || K < 0)
         return DETRED_EINVAL;
@@ -215,7 +215,7 @@ int auto_split(const Policy& p, int M, int N)
 }
 
 // Resolve split_k / tp_shards against the policy; 0 means auto_split.
-int resolve_split(const Policy& p, int split, int M, int N, int* out)
+detred_status resolve_split(const Policy& p, int split, int M, int N, int* out)
 {
     if (split == 0)
         split = auto_split(p, M, N);
@@ -229,7 +229,7 @@ int resolve_split(const Policy& p, int split, int M, int N, int* out)
 
 extern "C" {
 
-const char* detred_status_string(int status)
+const char* detred_status_string(detred_status status)
 {
     switch (status) {
     case DETRED_OK: return "DETRED_OK";
@@ -243,8 +243,8 @@ const char* detred_status_string(int status)
 
 int detred_version(void) { return 100; }
 
-int detred_policy(int N, int K, int* chunks, int* chunk_k, int* tile_m, int* tile_n,
-                  int* default_split)
+detred_status detred_policy(int N, int K, int* chunks, int* chunk_k, int* tile_m, int* tile_n,
+                            int* default_split)
 {
     if (N < 0 || K < 0)
         return DETRED_EINVAL;
@@ -271,12 +271,13 @@ size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards)
     const Policy p = plan(M, N, K);
     if (split_or_shards == 0)
         split_or_shards = auto_split(p, M, N);
-    if (!pow2_le8(split_or_shards) || split_or_shards == 1)
+    // no workspace for one slice, none for a split the calls reject
+    if (!pow2_le8(split_or_shards) || split_or_shards == 1 || split_or_shards > p.P)
         return 0;
     return partial_bytes(M, N, split_or_shards) + counter_bytes(p, M, N);
 }
 
-int detred_workspace_init(void* ws, size_t ws_bytes, detred_stream s)
+detred_status detred_workspace_init(void* ws, size_t ws_bytes, detred_stream s)
 {
     if (ws_bytes == 0)
         return DETRED_OK;
@@ -294,7 +295,7 @@ namespace {
 // S subtree roots into S planes [S][M][N] at ws (plain stores, one launch),
 // then the top log2(S) tree levels into Y (a second, streaming launch).
 // The bits are those of the one-launch last-arriver combine.
-int run_roots_then_combine(Policy p, GemmArgs g, int S, float* ws, hipStream_t hs)
+detred_status run_roots_then_combine(Policy p, GemmArgs g, int S, float* ws, hipStream_t hs)
 {
     const GemmArgs out = g;  // Y, ldy and the epilogue of the combined value
     g.Y = ws;
@@ -327,7 +328,8 @@ int run_roots_then_combine(Policy p, GemmArgs g, int S, float* ws, hipStream_t h
 // 9.8 -> 9.1 us; 16x16x512 at 8 6.8 us in one launch against 8.0 in two.
 constexpr size_t kTwoPhaseMinElems = 16384;
 
-int run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_bytes, hipStream_t hs)
+detred_status run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_bytes,
+                      hipStream_t hs)
 {
     Policy p = p0;
     if (g.K == 0)
@@ -353,7 +355,8 @@ int run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_bytes, hipS
 
 // Validation of det_splitk_gemm / det_splitk_addmm that would otherwise
 // only happen in run_det (so a composite call can check before launching).
-int check_det(const Policy& p, int M, int N, int K, int S, const void* ws, size_t ws_bytes)
+detred_status check_det(const Policy& p, int M, int N, int K, int S, const void* ws,
+                        size_t ws_bytes)
 {
     if (K == 0 || S == 1)
         return DETRED_OK;
@@ -364,7 +367,7 @@ int check_det(const Policy& p, int M, int N, int K, int S, const void* ws, size_
     return DETRED_OK;
 }
 
-int check_epilogue(const float* C, int ldc, int N, int y_dtype)
+detred_status check_epilogue(const float* C, int ldc, int N, int y_dtype)
 {
     if (y_dtype != DETRED_F32 && y_dtype != DETRED_BF16)
         return DETRED_EINVAL;
@@ -399,11 +402,11 @@ LoraLayout lora_layout(int M, int N, int K, int r)
 
 namespace {
 
-int det_gemm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* Y,
-                  int ldy, int M, int N, int K, int split_k, void* ws, size_t ws_bytes,
-                  detred_stream s)
+detred_status det_gemm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt,
+                            float* Y, int ldy, int M, int N, int K, int split_k, void* ws,
+                            size_t ws_bytes, detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, wt);
+    detred_status st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     const Policy p = plan(M, N, K);
@@ -415,11 +418,12 @@ int det_gemm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool w
     return run_det(p, g, S, ws, ws_bytes, (hipStream_t)s);
 }
 
-int det_addmm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt,
-                   const float* C, int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype,
-                   int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+detred_status det_addmm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt,
+                             const float* C, int ldc, float alpha, float beta, void* Y, int ldy,
+                             int y_dtype, int M, int N, int K, int split_k, void* ws,
+                             size_t ws_bytes, detred_stream s)
 {
-    int st = check_epilogue(C, ldc, N, y_dtype);
+    detred_status st = check_epilogue(C, ldc, N, y_dtype);
     if (st != DETRED_OK)
         return st;
     st = check_gemm(X, ldx, W, ldw, (const float*)Y, ldy, M, N, K, wt);
@@ -444,30 +448,33 @@ int det_addmm_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool 
 
 extern "C" {
 
-int det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
-                    int M, int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+detred_status det_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y,
+                              int ldy, int M, int N, int K, int split_k, void* ws, size_t ws_bytes,
+                              detred_stream s)
 {
     return det_gemm_impl(X, ldx, W, ldw, false, Y, ldy, M, N, K, split_k, ws, ws_bytes, s);
 }
 
-int det_splitk_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* Y,
-                       int ldy, int M, int N, int K, int split_k, void* ws, size_t ws_bytes,
-                       detred_stream s)
+detred_status det_splitk_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* Y,
+                                 int ldy, int M, int N, int K, int split_k, void* ws,
+                                 size_t ws_bytes, detred_stream s)
 {
     return det_gemm_impl(X, ldx, Wt, ldwt, true, Y, ldy, M, N, K, split_k, ws, ws_bytes, s);
 }
 
-int det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const float* C,
-                     int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype, int M, int N,
-                     int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+detred_status det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw,
+                               const float* C, int ldc, float alpha, float beta, void* Y, int ldy,
+                               int y_dtype, int M, int N, int K, int split_k, void* ws,
+                               size_t ws_bytes, detred_stream s)
 {
     return det_addmm_impl(X, ldx, W, ldw, false, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K,
                           split_k, ws, ws_bytes, s);
 }
 
-int det_splitk_addmm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, const float* C,
-                        int ldc, float alpha, float beta, void* Y, int ldy, int y_dtype, int M,
-                        int N, int K, int split_k, void* ws, size_t ws_bytes, detred_stream s)
+detred_status det_splitk_addmm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt,
+                                  const float* C, int ldc, float alpha, float beta, void* Y,
+                                  int ldy, int y_dtype, int M, int N, int K, int split_k, void* ws,
+                                  size_t ws_bytes, detred_stream s)
 {
     return det_addmm_impl(X, ldx, Wt, ldwt, true, C, ldc, alpha, beta, Y, ldy, y_dtype, M, N, K,
                           split_k, ws, ws_bytes, s);
@@ -480,9 +487,10 @@ size_t det_lora_workspace_bytes(int M, int N, int K, int r)
     return lora_layout(M, N, K, r).total;
 }
 
-int det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw, const uint16_t* A,
-                     int lda, const uint16_t* B, int ldb, float scale, uint16_t* Y, int ldy, int M,
-                     int N, int K, int r, void* ws, size_t ws_bytes, detred_stream s)
+detred_status det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw,
+                               const uint16_t* A, int lda, const uint16_t* B, int ldb, float scale,
+                               uint16_t* Y, int ldy, int M, int N, int K, int r, void* ws,
+                               size_t ws_bytes, detred_stream s)
 {
     if (M < 0 || N < 0 || K < 0 || r <= 0)
         return DETRED_EINVAL;
@@ -498,7 +506,7 @@ int det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
     uint16_t* zb = (uint16_t*)(w + l.zb);
     const Policy pb = plan(M, N, K), pz = plan(M, r, K), pe = plan(M, N, r);
     // every check before the first launch
-    int st;
+    detred_status st;
     if ((st = check_gemm(X, ldx, W, ldw, base, N, M, N, K)) != DETRED_OK ||
         (st = check_gemm(X, ldx, A, lda, (const float*)zb, r, M, r, K)) != DETRED_OK ||
         (st = check_gemm(zb, r, B, ldb, (const float*)Y, ldy, M, N, r)) != DETRED_OK ||
@@ -526,10 +534,10 @@ int det_lora_forward(const uint16_t* X, int ldx, const uint16_t* W, int ldw, con
     return run_det(pe, ge, 1, nullptr, 0, hs);
 }
 
-int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
-                       int M, int N, int K, int split_k, detred_stream s)
+detred_status atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y,
+                                 int ldy, int M, int N, int K, int split_k, detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    detred_status st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     const Policy p = plan(M, N, K);
@@ -550,11 +558,11 @@ int atomic_splitk_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, f
 
 namespace {
 
-int tree_tp_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* Y,
-                 int ldy, int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes,
-                 detred_stream s)
+detred_status tree_tp_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt,
+                           float* Y, int ldy, int M, int N, int K, int tp_shards, void* ws,
+                           size_t ws_bytes, detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, wt);
+    detred_status st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     Policy p = plan(M, N, K);
@@ -577,10 +585,10 @@ int tree_tp_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt
     return run_roots_then_combine(p, g, T, (float*)ws, hs);
 }
 
-int tree_tp_shards_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt, float* P,
-                        int M, int N, int K, int tp_shards, detred_stream s)
+detred_status tree_tp_shards_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, bool wt,
+                                  float* P, int M, int N, int K, int tp_shards, detred_stream s)
 {
-    int st = check_gemm(X, ldx, W, ldw, P, N, M, N, K, wt);
+    detred_status st = check_gemm(X, ldx, W, ldw, P, N, M, N, K, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     Policy p = plan(M, N, K);
@@ -599,8 +607,9 @@ int tree_tp_shards_impl(const uint16_t* X, int ldx, const uint16_t* W, int ldw, 
     return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P / tp_shards, hs));
 }
 
-int tree_tp_shard_impl(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, bool wt,
-                       float* Pt, int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+detred_status tree_tp_shard_impl(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, bool wt,
+                                 float* Pt, int ldp, int M, int N, int Kt, int tp_shards,
+                                 detred_stream s)
 {
     if (!pow2_le8(tp_shards) || Kt < 0)
         return DETRED_EINVAL;
@@ -608,7 +617,7 @@ int tree_tp_shard_impl(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
     if (Kl > 0x7fffffffL)
         return DETRED_EINVAL;
     const int K = (int)Kl;
-    int st = check_gemm(Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, wt);
+    detred_status st = check_gemm(Xt, ldx, Wt, ldw, Pt, ldp, M, N, Kt, wt);
     if (st != DETRED_OK || M == 0 || N == 0)
         return st;
     Policy p = plan(M, N, K);
@@ -629,45 +638,48 @@ int tree_tp_shard_impl(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
 
 extern "C" {
 
-int tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y, int ldy,
-                 int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes, detred_stream s)
+detred_status tree_tp_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* Y,
+                           int ldy, int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes,
+                           detred_stream s)
 {
     return tree_tp_impl(X, ldx, W, ldw, false, Y, ldy, M, N, K, tp_shards, ws, ws_bytes, s);
 }
 
-int tree_tp_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* Y, int ldy,
-                    int M, int N, int K, int tp_shards, void* ws, size_t ws_bytes,
-                    detred_stream s)
+detred_status tree_tp_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* Y,
+                              int ldy, int M, int N, int K, int tp_shards, void* ws,
+                              size_t ws_bytes, detred_stream s)
 {
     return tree_tp_impl(X, ldx, Wt, ldwt, true, Y, ldy, M, N, K, tp_shards, ws, ws_bytes, s);
 }
 
-int tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* P, int M,
-                        int N, int K, int tp_shards, detred_stream s)
+detred_status tree_tp_shards_gemm(const uint16_t* X, int ldx, const uint16_t* W, int ldw, float* P,
+                                  int M, int N, int K, int tp_shards, detred_stream s)
 {
     return tree_tp_shards_impl(X, ldx, W, ldw, false, P, M, N, K, tp_shards, s);
 }
 
-int tree_tp_shards_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt, float* P,
-                           int M, int N, int K, int tp_shards, detred_stream s)
+detred_status tree_tp_shards_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt, int ldwt,
+                                     float* P, int M, int N, int K, int tp_shards, detred_stream s)
 {
     return tree_tp_shards_impl(X, ldx, Wt, ldwt, true, P, M, N, K, tp_shards, s);
 }
 
-int tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw, float* Pt,
-                       int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+detred_status tree_tp_shard_gemm(const uint16_t* Xt, int ldx, const uint16_t* Wt, int ldw,
+                                 float* Pt, int ldp, int M, int N, int Kt, int tp_shards,
+                                 detred_stream s)
 {
     return tree_tp_shard_impl(Xt, ldx, Wt, ldw, false, Pt, ldp, M, N, Kt, tp_shards, s);
 }
 
-int tree_tp_shard_gemm_wt(const uint16_t* Xt, int ldx, const uint16_t* Wtt, int ldwt, float* Pt,
-                          int ldp, int M, int N, int Kt, int tp_shards, detred_stream s)
+detred_status tree_tp_shard_gemm_wt(const uint16_t* Xt, int ldx, const uint16_t* Wtt, int ldwt,
+                                    float* Pt, int ldp, int M, int N, int Kt, int tp_shards,
+                                    detred_stream s)
 {
     return tree_tp_shard_impl(Xt, ldx, Wtt, ldwt, true, Pt, ldp, M, N, Kt, tp_shards, s);
 }
 
-int tree_combine_f32(const float* parts, size_t part_stride, int count, float* Y, size_t n,
-                     detred_stream s)
+detred_status tree_combine_f32(const float* parts, size_t part_stride, int count, float* Y,
+                               size_t n, detred_stream s)
 {
     if (!pow2_le8(count))
         return DETRED_EUNSUPPORTED;
@@ -679,7 +691,7 @@ int tree_combine_f32(const float* parts, size_t part_stride, int count, float* Y
     return hip_status(launch_tree_combine(parts, part_stride, count, Y, n, (hipStream_t)s));
 }
 
-int detred_f32_to_bf16(const float* x, uint16_t* y, size_t n, detred_stream s)
+detred_status detred_f32_to_bf16(const float* x, uint16_t* y, size_t n, detred_stream s)
 {
     if (n == 0)
         return DETRED_OK;
@@ -690,8 +702,8 @@ int detred_f32_to_bf16(const float* x, uint16_t* y, size_t n, detred_stream s)
     return hip_status(launch_cast_bf16(x, y, n, (hipStream_t)s));
 }
 
-int inv_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows, int hidden,
-                float eps, detred_stream s)
+detred_status inv_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows, int hidden,
+                          float eps, detred_stream s)
 {
     if (rows < 0 || hidden < 0)
         return DETRED_EINVAL;
@@ -704,8 +716,8 @@ int inv_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows, in
     return hip_status(launch_rmsnorm(x, gamma, y, rows, hidden, eps, (hipStream_t)s));
 }
 
-int inv_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int rows, int hidden,
-                     float eps, detred_stream s)
+detred_status inv_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int rows,
+                               int hidden, float eps, detred_stream s)
 {
     if (rows < 0 || hidden < 0)
         return DETRED_EINVAL;
@@ -718,7 +730,7 @@ int inv_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int 
     return hip_status(launch_rmsnorm_bf16(x, gamma, y, rows, hidden, eps, (hipStream_t)s));
 }
 
-int inv_log_softmax(const float* x, float* y, int rows, int cols, detred_stream s)
+detred_status inv_log_softmax(const float* x, float* y, int rows, int cols, detred_stream s)
 {
     if (rows < 0 || cols < 0)
         return DETRED_EINVAL;
@@ -731,7 +743,8 @@ int inv_log_softmax(const float* x, float* y, int rows, int cols, detred_stream 
     return hip_status(launch_log_softmax(x, y, rows, cols, (hipStream_t)s));
 }
 
-int inv_log_softmax_mean(const float* x, float* y, float* mu, int rows, int cols, detred_stream s)
+detred_status inv_log_softmax_mean(const float* x, float* y, float* mu, int rows, int cols,
+                                   detred_stream s)
 {
     if (rows < 0 || cols < 0)
         return DETRED_EINVAL;
@@ -744,7 +757,7 @@ int inv_log_softmax_mean(const float* x, float* y, float* mu, int rows, int cols
     return hip_status(launch_log_softmax_mean(x, y, mu, rows, cols, (hipStream_t)s));
 }
 
-int inv_mean(const float* x, float* y, int rows, int cols, detred_stream s)
+detred_status inv_mean(const float* x, float* y, int rows, int cols, detred_stream s)
 {
     if (rows < 0 || cols < 0)
         return DETRED_EINVAL;
@@ -766,10 +779,11 @@ size_t inv_decode_attention_workspace_bytes(int B, int Hq, int D, int max_len)
     return round_up(rows * D * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
 }
 
-int inv_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long kv_stride_b,
-                         long kv_stride_h, long kv_stride_t, const int* lens, float* out, int B,
-                         int Hq, int Hkv, int D, int max_len, float scale, void* ws,
-                         size_t ws_bytes, detred_stream s)
+detred_status inv_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   long kv_stride_b, long kv_stride_h, long kv_stride_t,
+                                   const int* lens, float* out, int B, int Hq, int Hkv, int D,
+                                   int max_len, float scale, void* ws, size_t ws_bytes,
+                                   detred_stream s)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || Hq % Hkv != 0)
         return DETRED_EINVAL;

@@ -88,6 +88,9 @@ def test_workspace_bytes():
     n = detred.detred_gemm_workspace_bytes(16, 16, 512, 8)
     assert n >= 8 * 16 * 16 * 4 + 4 and n % 256 == 0
     assert detred.detred_gemm_workspace_bytes(16, 16, 512, 3) == 0
+    # a split the products reject needs no workspace either (one chunk: P = 1)
+    assert detred.detred_gemm_workspace_bytes(16, 16, 264, 2) == 0
+    assert detred.detred_gemm_workspace_bytes(16, 4096, 64, 8) == 0
 
 
 A16 = 0x10000          # fake, 16-byte aligned addresses: never dereferenced
