@@ -114,7 +114,9 @@ def _entry(marshal):
 
 def prepare(fn, *args, **kw):
     """Marshal once; return a zero-argument callable that issues the same C
-    call (same pointers, sizes and stream) each time it is called."""
+    call (same pointers, sizes and stream) each time it is called.  The
+    callable holds references to the tensors it was given (a workspace
+    created inline stays allocated as long as the callable exists)."""
     name, cargs = fn.marshal(*args, **kw)
     cfun = getattr(lib(), name)
 
@@ -122,6 +124,7 @@ def prepare(fn, *args, **kw):
         st = cfun(*cargs)
         if st != OK:
             raise DetredError(st, name)
+    launch.tensors = (args, kw)
     return launch
 
 
