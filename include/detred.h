@@ -205,6 +205,29 @@ detred_status det_splitk_addmm_wt(const uint16_t *X, int ldx, const uint16_t *Wt
                                   size_t ws_bytes, detred_stream s);
 
 /*
+ * det_splitk_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same product, split rules and output bits as det_splitk_gemm, with no
+ * workspace argument: the S slice partials and the arrival counters live in
+ * a scratch array the library holds on each device it runs on (32 MiB,
+ * kept until the process ends).  The first call on a device looks the
+ * array up with that device current and zeroes its counters with a kernel
+ * on s; no call allocates or frees memory (no hipMalloc, hipFree or
+ * allocating library routine).
+ * Limit: with S > 1 the partials, S*M*N*4 bytes, must not exceed
+ * DETRED_NOALLOC_PARTIAL_BYTES (EWORKSPACE otherwise, nothing launched).
+ * S == 1 and K == 0 use no scratch.  Every call on a device shares its
+ * scratch: calls that overlap on one device (other streams, other host
+ * threads) race and give undefined results; calls ordered on one stream, or
+ * synchronised, do not.  Other arguments and errors as det_splitk_gemm.
+ */
+#define DETRED_NOALLOC_PARTIAL_BYTES ((size_t)33488896) /* 32 MiB - 64 KiB */
+detred_status det_splitk_gemm_noalloc(const uint16_t *X, int ldx,
+                                      const uint16_t *W, int ldw, float *Y,
+                                      int ldy, int M, int N, int K, int split_k,
+                                      detred_stream s);
+
+/*
  * Workspace of det_lora_forward for an M x N layer output with input width K
  * and LoRA rank r: the fp32 base product, the bf16 shrink output and the
  * split-K workspaces of the base product and the shrink, each 256-byte

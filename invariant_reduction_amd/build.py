@@ -19,7 +19,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdetred.so")
 ARCH = os.environ.get("DETRED_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gemm.hip", "gemm_lds.hip", "rows.hip", "attention.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "gemm_lds.hip", "rows.hip", "attention.hip", "noalloc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

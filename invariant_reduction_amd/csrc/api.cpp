@@ -328,8 +328,11 @@ detred_status run_roots_then_combine(Policy p, GemmArgs g, int S, float* ws, hip
 // 9.8 -> 9.1 us; 16x16x512 at 8 6.8 us in one launch against 8.0 in two.
 constexpr size_t kTwoPhaseMinElems = 16384;
 
+// counters: where the arrival counters of a last-arriver combine live when
+// not in ws after the partials (the no-allocation entry point keeps them at
+// a fixed place in its scratch, so that they stay zero between calls).
 detred_status run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_bytes,
-                      hipStream_t hs)
+                      hipStream_t hs, unsigned* counters = nullptr)
 {
     Policy p = p0;
     if (g.K == 0)
@@ -342,13 +345,13 @@ detred_status run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_b
     // the last-arriver combine addresses a tile's rows with 32-bit offsets
     if ((size_t)(p.bm - 1) * g.N + p.bn >= ((size_t)1 << 29))
         return DETRED_EUNSUPPORTED;
-    const size_t need = partial_bytes(g.M, g.N, S) + counter_bytes(p, g.M, g.N);
+    const size_t need = partial_bytes(g.M, g.N, S) + (counters ? 0 : counter_bytes(p, g.M, g.N));
     if (!ws || !aligned256(ws) || ws_bytes < need)
         return DETRED_EWORKSPACE;
     if (p.tile == TILE_L128 || (size_t)g.M * g.N >= kTwoPhaseMinElems)
         return run_roots_then_combine(p, g, S, (float*)ws, hs);
     g.part = (float*)ws;
-    g.counters = (unsigned*)((char*)ws + partial_bytes(g.M, g.N, S));
+    g.counters = counters ? counters : (unsigned*)((char*)ws + partial_bytes(g.M, g.N, S));
     narrow_for_decode(p, g, p.P / S);
     return hip_status(launch_slice_gemm(p.tile, EPI_COMBINE, g, p.P / S, hs));
 }
@@ -460,6 +463,38 @@ detred_status det_splitk_gemm_wt(const uint16_t* X, int ldx, const uint16_t* Wt,
                                  size_t ws_bytes, detred_stream s)
 {
     return det_gemm_impl(X, ldx, Wt, ldwt, true, Y, ldy, M, N, K, split_k, ws, ws_bytes, s);
+}
+
+static_assert(kNoallocScratchBytes - kNoallocCounterBytes == DETRED_NOALLOC_PARTIAL_BYTES,
+              "the header states the no-allocation limit");
+
+detred_status det_splitk_gemm_noalloc(const uint16_t* X, int ldx, const uint16_t* W, int ldw,
+                                      float* Y, int ldy, int M, int N, int K, int split_k,
+                                      detred_stream s)
+{
+    detred_status st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+    if (st != DETRED_OK || M == 0 || N == 0)
+        return st;
+    const Policy p = plan(M, N, K);
+    int S = 0;
+    if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
+        return st;
+    hipStream_t hs = (hipStream_t)s;
+    const GemmArgs g = make_args(p, X, ldx, W, ldw, Y, ldy, M, N, K, S);
+    if (K == 0 || S == 1)
+        return run_det(p, g, S, nullptr, 0, hs);  // no scratch involved
+    if (partial_bytes(M, N, S) > kNoallocScratchBytes - kNoallocCounterBytes ||
+        counter_bytes(p, M, N) > kNoallocCounterBytes)
+        return DETRED_EWORKSPACE;
+    if ((size_t)(p.bm - 1) * N + p.bn >= ((size_t)1 << 29))
+        return DETRED_EUNSUPPORTED;
+    void* scratch = nullptr;
+    if (noalloc_scratch(hs, &scratch) != hipSuccess)
+        return DETRED_EHIP;
+    char* base = static_cast<char*>(scratch);
+    return run_det(p, g, S, base + kNoallocCounterBytes,
+                   kNoallocScratchBytes - kNoallocCounterBytes, hs,
+                   reinterpret_cast<unsigned*>(base));
 }
 
 detred_status det_splitk_addmm(const uint16_t* X, int ldx, const uint16_t* W, int ldw,

@@ -82,6 +82,15 @@ hipError_t launch_tree_combine_rows(const float* parts, size_t stride, int count
 hipError_t launch_fill_zero(float* Y, long ld, int M, int N, hipStream_t s);
 hipError_t launch_cast_bf16(const float* x, uint16_t* y, size_t n, hipStream_t s);
 
+// Scratch of det_splitk_gemm_noalloc (noalloc.hip): a file-scope device
+// array per device.  Counters at offset 0 (zero at rest), the partials
+// after them.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+constexpr size_t kNoallocCounterBytes = (size_t)64 << 10;
+// The device address of the current device's scratch; the first call on a
+// device looks it up and zeroes its counters on stream s.
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
+
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float* y, int rows,
                           int hidden, float eps, hipStream_t s);
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int rows,

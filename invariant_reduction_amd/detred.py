@@ -40,6 +40,7 @@ SIGNATURES = {
     "det_splitk_gemm_wt": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "det_splitk_addmm_wt": ([_P, _I, _P, _I, _P, _I, _F, _F, _P, _I, _I, _I, _I, _I, _I, _P, _Z,
                              _P], _I),
+    "det_splitk_gemm_noalloc": ([_P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P], _I),
     "det_lora_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "det_lora_forward": ([_P, _I, _P, _I, _P, _I, _P, _I, _F, _P, _I, _I, _I, _I, _I, _P, _Z,
                           _P], _I),
@@ -236,6 +237,19 @@ def det_splitk_gemm(X, W, Y, split_k=0, ws=None, stream=None):
     pws, nws = _ws(ws)
     return ("det_splitk_gemm_wt" if wt else "det_splitk_gemm"), (
         px, ldx, pw, ldw, py, ldy, M, N, K, split_k, pws, nws, _stream(stream))
+
+
+@_entry
+def det_splitk_gemm_noalloc(X, W, Y, split_k=0, stream=None):
+    """det_splitk_gemm with no workspace argument: the partials live in the
+    library's per-device scratch (for callers that cannot allocate).  W is a
+    row-major [K, N] matrix.  Same bits as det_splitk_gemm."""
+    px, ldx = _mat(X, _BF16_TYPES, "X")
+    pw, ldw = _mat(W, _BF16_TYPES, "W")
+    py, ldy = _mat(Y, (torch.float32,), "Y")
+    M, N, K = _gemm_dims(X, W, Y)
+    return "det_splitk_gemm_noalloc", (px, ldx, pw, ldw, py, ldy, M, N, K, split_k,
+                                       _stream(stream))
 
 
 @_entry

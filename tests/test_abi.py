@@ -129,6 +129,28 @@ def test_det_splitk_rejects(kw, status):
     assert call_det(**kw) == status
 
 
+def test_noalloc_entry_point_rejects_before_any_gpu_work():
+    L = detred.lib()
+
+    def na(**kw):
+        a = dict(X=A16, ldx=512, W=A16b, ldw=16, Y=A16c, ldy=16, M=16, N=16, K=512, S=8)
+        a.update(kw)
+        return L.det_splitk_gemm_noalloc(a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"],
+                                         a["M"], a["N"], a["K"], a["S"], None)
+    assert na(M=-1) == detred.EINVAL
+    assert na(X=MIS) == detred.EINVAL
+    assert na(ldy=8) == detred.EINVAL
+    assert na(S=3) == detred.EUNSUPPORTED
+    assert na(K=264, ldx=264, S=2) == detred.EUNSUPPORTED
+    assert na(M=0, X=None, W=None, Y=None) == detred.OK
+    # partials beyond the scratch: 8 x 4096 x 4096 fp32 = 512 MiB, and the
+    # first size past the limit (8 planes of 1024 x 1024 = 32 MiB)
+    big = dict(ldx=4096, ldw=4096, ldy=4096, M=4096, N=4096, K=4096, S=8)
+    assert na(**big) == detred.EWORKSPACE
+    assert na(**dict(big, M=1024, N=1024, ldw=1024, ldy=1024)) == detred.EWORKSPACE
+    assert 8 * 1024 * 1016 * 4 <= 33488896 < 8 * 1024 * 1024 * 4
+
+
 def test_transposed_weight_entry_points_reject():
     L = detred.lib()
     f = ctypes.c_float
