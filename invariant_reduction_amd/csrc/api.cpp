@@ -173,6 +173,46 @@ void narrow_for_decode(Policy& p, GemmArgs& g, int cps)
     g = w;
 }
 
+// Eight-chunk products of 1024 rows or more on the 192x128 tile (MI355X:
+// 1024 rows of 4096x14336 205 -> 196 us, 4096 rows 635 -> 621 us), whose
+// top subtree level waits in the product's own output rows of Y
+// (so the output must be fp32 and hold nothing the call still reads: no
+// bf16 output, and a C that overlaps Y keeps the 128x128 tile).  The tile
+// never changes the bits.
+constexpr int kWideMinRows = 1024;
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+void widen_for_rows(Policy& p, GemmArgs& g, int cps)
+{
+    if (p.tile != TILE_L128 || cps != 8 || g.M < kWideMinRows || g.out_z_stride != 0)
+        return;
+    if (g.epi && g.out_bf16)
+        return;
+    if (g.epi && g.C) {
+        const size_t ybytes = ((size_t)(g.M - 1) * g.ldy + g.N) * sizeof(float);
+        const size_t cbytes =
+            (g.ldc == 0 ? (size_t)g.N : (size_t)(g.M - 1) * g.ldc + g.N) * sizeof(float);
+        if (overlaps(g.Y, ybytes, g.C, cbytes))
+            return;
+    }
+    GemmArgs w = g;
+    int bm = 0, bn = 0;
+    tile_shape(TILE_W256, &bm, &bn);
+    w.tiles_m = (g.M + bm - 1) / bm;
+    w.tiles_n = (g.N + bn - 1) / bn;
+    if (!lds_engine_supports(TILE_W256, w, cps))
+        return;
+    p.tile = TILE_W256;
+    p.bm = bm;
+    p.bn = bn;
+    g = w;
+}
+
 // The split for split_k = 0.  The split only decides how many workgroups
 // share the chunk tree, never the bits.  Narrow outputs keep the policy's
 // split (one slice per chunk).  A wide product is sized against the 256 CUs,
@@ -340,6 +380,7 @@ detred_status run_det(const Policy& p0, GemmArgs g, int S, void* ws, size_t ws_b
                                 : launch_fill_zero(g.Y, g.ldy, g.M, g.N, hs));
     if (S == 1) {
         narrow_for_decode(p, g, p.P);
+        widen_for_rows(p, g, p.P);
         return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
     }
     // the last-arriver combine addresses a tile's rows with 32-bit offsets
@@ -611,6 +652,7 @@ detred_status tree_tp_impl(const uint16_t* X, int ldx, const uint16_t* W, int ld
     g.wt = wt;
     if (T == 1) {
         narrow_for_decode(p, g, p.P);
+        widen_for_rows(p, g, p.P);
         return hip_status(launch_slice_gemm(p.tile, EPI_STORE, g, p.P, hs));
     }
     if (!ws || !aligned256(ws) || ws_bytes < partial_bytes(M, N, T))

@@ -84,6 +84,15 @@ using Tile256 = LdsTile<256, 256, 2, 4>;
 // HBM: 41.0 -> 32.6 us against 128x128; a 32x128 tile was no faster
 // below 32 rows).
 using TileD64 = LdsTile<64, 128, 2, 4>;
+// Eight-chunk products of 1024 rows or more: 192x128, eight waves of 96x32
+// (two per SIMD).  Half again the rows of the 128x128 tile per workgroup,
+// so each weight block in LDS serves 1.5 times the MFMAs and the LDS bytes
+// per MFMA drop by a fifth; the cost is 48 more accumulator registers per
+// saved subtree level, which fit because the top level waits in the
+// workgroup's own output tile of Y between chunk 3 and chunk 7 (the call
+// needs no workspace).  Measured on MI355X against the 128x128 tile: 1024
+// rows of 4096x14336 205 -> 196 us, 4096 rows 635 -> 621 us.
+using TileW = LdsTile<192, 128, 2, 4>;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -130,6 +139,23 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, const i3
 #pragma clang diagnostic pop
 }
 
+
+// dma16 with a wave-uniform part of the offset in an SGPR: the load reads
+// the buffer at voff + soff.
+__device__ __forceinline__ void dma16s(uint32_t lds_base, uint32_t voff, uint32_t soff,
+                                       const i32x4& desc)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(desc), "s"(soff)
+        : "memory", "m0");
+#pragma clang diagnostic pop
+}
 
 // s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
 __device__ __forceinline__ void wait_lgkmcnt0()
@@ -386,6 +412,92 @@ __device__ __forceinline__ void store_roots_direct(const f32x4 (&acc)[T::FM][T::
             }
 }
 
+// The top subtree level parked in the workgroup's own output tile of Y
+// (PARK == 2): written once after chunk 3 and read back once after chunk 7,
+// by the lane that wrote it.  A tile that lies wholly inside M x N holds
+// the level as whole 16-byte pieces in an order of its own (lane slot s of
+// block (fm, fn) of wave w, s = ((w*FM + fm)*FN + fn)*64 + lane, at tile
+// row s/(BN/4), column 4*(s%(BN/4))); an edge tile keeps every value at
+// its own element, and the buffer's range check drops (and reads as zero)
+// the ones outside M x N, which no later step uses.  The final store
+// overwrites the whole tile.
+template <class T>
+struct ParkOut {
+    __amdgpu_buffer_rsrc_t rs;  // based at the tile's first element of Y
+    bool full;                  // the tile lies wholly inside M x N
+    int ld;                     // Y's row stride in elements
+    int rows_left, cols_left;   // M - row0, N - col0
+    int wave, wrow, wcol;       // wave index, its first row and column in the tile
+};
+
+template <class T>
+__device__ __forceinline__ void park_out_store(const ParkOut<T>& po, const f32x4 (&v)[T::FM][T::FN],
+                                               int lane_in)
+{
+    constexpr int OOB = (int)0x80000000u;
+    // the lane index made opaque, so that the store offsets are computed
+    // here rather than hoisted out of the K loops (where they would hold
+    // registers for the whole kernel)
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+            if (po.full) {
+                const int sl = ((po.wave * T::FM + fm) * T::FN + fn) * 64 + lane;
+                const int off = ((sl / (T::BN / 4)) * po.ld + 4 * (sl % (T::BN / 4))) * 4;
+                const u32x4 q = {__float_as_uint(v[fm][fn][0]), __float_as_uint(v[fm][fn][1]),
+                                 __float_as_uint(v[fm][fn][2]), __float_as_uint(v[fm][fn][3])};
+                __builtin_amdgcn_raw_buffer_store_b128(q, po.rs, off, 0, CPOL_NT);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = po.wrow + fm * 16 + 4 * (lane >> 4) + q;
+                    const int c = po.wcol + fn * 16 + (lane & 15);
+                    const bool in = r < po.rows_left && c < po.cols_left;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[fm][fn][q]), po.rs,
+                                                          in ? (r * po.ld + c) * 4 : OOB, 0,
+                                                          CPOL_NT);
+                }
+            }
+        }
+}
+
+// acc = parked + acc, element by element (the tree node's left operand is
+// the parked level)
+template <class T>
+__device__ __forceinline__ void park_out_add(const ParkOut<T>& po, f32x4 (&acc)[T::FM][T::FN],
+                                             int lane_in)
+{
+    constexpr int OOB = (int)0x80000000u;
+    int lane = lane_in;  // opaque, as in park_out_store
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+            f32x4 left;
+            if (po.full) {
+                const int sl = ((po.wave * T::FM + fm) * T::FN + fn) * 64 + lane;
+                const int off = ((sl / (T::BN / 4)) * po.ld + 4 * (sl % (T::BN / 4))) * 4;
+                const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(po.rs, off, 0, 0);
+                left = f32x4{__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
+                             __uint_as_float(q.w)};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = po.wrow + fm * 16 + 4 * (lane >> 4) + q;
+                    const int c = po.wcol + fn * 16 + (lane & 15);
+                    const bool in = r < po.rows_left && c < po.cols_left;
+                    left[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        po.rs, in ? (r * po.ld + c) * 4 : OOB, 0, 0));
+                }
+            }
+            acc[fm][fn] = left + acc[fm][fn];
+        }
+}
+
 template <class T, int STAGES, int CPS, int EPI, bool PARK, bool WT>
 __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
 {
@@ -581,7 +693,7 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
         // EPI_STORE: the final product, or slice tc.z's subtree root in its
         // own plane (out_z_stride)
         float* out = g.Y + (size_t)tc.z * g.out_z_stride;
-        if constexpr (T::BM == 256) {
+        if constexpr (T::BM == 256 && T::BN == 256) {
             // the root tile: plain roots only, never an addmm epilogue (the
             // direct form only with a row-major W: beside the transposed
             // operand's addressing it would not fit the registers)
@@ -597,6 +709,283 @@ __global__ __launch_bounds__(T::THREADS) void lds_gemm_kernel(GemmArgs g)
             store_tile_via_lds<T, STAGES>(acc, g, out, g.ldy, row0, col0, wm, wn, lane, tid, smem);
         }
     }
+}
+
+// Eight-chunk product on the 192x128 tile (TileW).  The same chunk chains
+// and tree as lds_gemm_kernel, arranged for the larger wave tile:
+//  * one MFMA target (acc) and two saved subtree levels (keep0, keep1):
+//    after chunk c the running value is added to the saved left siblings
+//    and saved, the binary counter of fold_chunk written out for eight
+//    chunks, with level 2 ((c0+c1)+(c2+c3)) parked in the output tile
+//    (ParkOut) from chunk 3 to chunk 7; each chunk has a K loop of its own;
+//  * A fragments rolled: the register of row fm takes the next k step's row
+//    fm right after its last MFMA of this step; B fragments double-buffered;
+//  * the LDS-DMA loads take their wave-uniform offset in a scalar register,
+//    so a lane keeps three offset registers instead of one per load;
+//  * no per-wave activity test and two k steps in every block (Kc % 64 ==
+//    0): the K loops have no branch around their MFMAs.
+template <class T, int STAGES, bool WT>
+__global__ __launch_bounds__(T::THREADS) void wide_gemm_kernel(GemmArgs g)
+{
+    constexpr int BM = T::BM, BN = T::BN, TM = T::TM, TN = T::TN, FM = T::FM, FN = T::FN;
+    constexpr int LOADS_A = T::LOADS_A, LOADS_B = T::LOADS_B;
+    constexpr int A_BYTES = T::A_BYTES, STAGE_BYTES = T::STAGE_BYTES;
+    constexpr int CPS = 8;
+    static_assert(FN <= FM, "B fragment reads ride on the first FN rows");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const TileCoord tc = tile_coord(g, BM, BN);
+    const int row0 = tc.row0, col0 = tc.col0;
+
+    const int rows_valid = (g.M - row0) < BM ? (g.M - row0) : BM;
+    const int cols_valid = (g.N - col0) < BN ? (g.N - col0) : BN;
+    const uint16_t* xa = g.X + (size_t)row0 * g.ldx;
+    const uint16_t* wb = WT ? g.W + (size_t)col0 * g.ldw : g.W + col0;
+    const uint32_t a_bytes = (uint32_t)(((size_t)(rows_valid - 1) * g.ldx + g.K) * 2);
+    const uint32_t b_bytes =
+        WT ? (uint32_t)(((size_t)(cols_valid - 1) * g.ldw + g.K) * 2)
+           : (uint32_t)(((size_t)(g.K - 1) * g.ldw + (g.N - col0)) * 2);
+    const i32x4 ra = buffer_desc(xa, a_bytes);
+    const i32x4 rb = buffer_desc(wb, b_bytes);
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)((DETRED_LDS uint8_t*)smem);
+
+    // Per-lane load offsets, as in lds_gemm_kernel, split into a per-lane
+    // part (in at most three registers) and a wave-uniform part passed as
+    // the scalar offset.  Load i of wave w fills 16-byte slots
+    // (w*LOADS + i)*64 + lane of the block:
+    //  A (and a transposed W): row (w*LOADS + i)*8 + lane/8, 16-byte chunk
+    //    (lane%8) ^ ((lane/8)%8) -- the row's low three bits come from lane;
+    //  W: k-row (w*LOADS_B + i)*4 + lane/16, chunk (lane%16) ^ b_swz(k), whose
+    //    bit ((w*LOADS_B + i)/2)%2 (wave-uniform) picks one of two per-lane
+    //    parts.
+    static_assert(T::B_ROW_CHUNKS == 16 && LOADS_B % 2 == 0, "B layout of the 128-wide tile");
+    const uint32_t va = (uint32_t)((((lane >> 3) * g.ldx) + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+    uint32_t vb0, vb1;
+    if constexpr (WT) {
+        vb0 = vb1 = (uint32_t)((((lane >> 3) * g.ldw) + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+    } else {
+        const int q = lane >> 4;
+        vb0 = (uint32_t)((q * g.ldw + 8 * ((lane & 15) ^ (2 * q))) * 2);
+        vb1 = (uint32_t)((q * g.ldw + 8 * ((lane & 15) ^ (2 * (q + 4)))) * 2);
+    }
+    const uint32_t lda_bytes = (uint32_t)g.ldx * 2, ldw_bytes = (uint32_t)g.ldw * 2;
+
+    const int nb = (g.Kc + BK - 1) / BK;
+    const int total = CPS * nb;
+    auto block_k = [&](int t) { return (t / nb) * g.Kc + (t % nb) * BK; };
+    auto issue = [&](int t) {
+        const uint32_t kb = (uint32_t)block_k(t);
+        const uint32_t st = smem_lds + (uint32_t)((t % STAGES) * STAGE_BYTES);
+#pragma unroll
+        for (int i = 0; i < LOADS_A; ++i)
+            dma16s(st + (uint32_t)((wave * LOADS_A + i) * 1024), va,
+                   (uint32_t)((wave * LOADS_A + i) * 8) * lda_bytes + kb * 2, ra);
+#pragma unroll
+        for (int i = 0; i < LOADS_B; ++i) {
+            const uint32_t so =
+                WT ? (uint32_t)((wave * LOADS_B + i) * 8) * ldw_bytes + kb * 2
+                   : ((uint32_t)((wave * LOADS_B + i) * 4) + kb) * ldw_bytes;
+            dma16s(st + (uint32_t)(A_BYTES + (wave * LOADS_B + i) * 1024),
+                   (((wave * LOADS_B + i) >> 1) & 1) ? vb1 : vb0, so, rb);
+        }
+    };
+    constexpr int LOADS_PER_ISSUE = LOADS_A + LOADS_B;
+
+    // fragment addresses inside a stage, as in lds_gemm_kernel
+    const int gq = lane >> 4, j = lane & 15;
+    uint32_t a_addr[KSTEPS], bt_addr[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        a_addr[ks] = (uint32_t)(((wm * TM + j) * 8 + ((4 * ks + gq) ^ (lane & 7))) * 16);
+        bt_addr[ks] = (uint32_t)(A_BYTES + ((wn * TN + j) * 8 + ((4 * ks + gq) ^ (lane & 7))) * 16);
+    }
+    uint32_t b_addr[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int rr = j >> 2, p = j & 3;
+        const int k = 8 * gq + rr;
+        const int n = wn * TN + fn * 16 + 4 * p;
+        const int chunk = (n >> 3) ^ (2 * (rr + 4 * (gq & 1)));
+        b_addr[fn] = (uint32_t)(A_BYTES + (k * T::B_ROW_CHUNKS + chunk) * 16 + ((n >> 2) & 1) * 8);
+    }
+    constexpr int ROW = BN * 2;  // bytes per k-row of a [k][n] B block
+    auto read_a = [&](const uint8_t* st, int ks, int fm) {
+        return *reinterpret_cast<const bf16x8*>(st + a_addr[ks] + fm * 16 * 8 * 16);
+    };
+    auto read_b = [&](const uint8_t* st, int ks, int fn) {
+        if constexpr (WT) {
+            return *reinterpret_cast<const bf16x8*>(st + bt_addr[ks] + fn * 16 * 8 * 16);
+        } else {
+            const uint8_t* pb = st + b_addr[fn] + ks * 32 * ROW;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb));
+            const v4i16 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((DETRED_LDS v4i16*)(pb + 4 * ROW));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    // One k step: the MFMAs of the fragments in af/bc, row by row; after row
+    // fm, af[fm] takes row fm of the next step (st_n, ks_n) and, for the
+    // first FN rows, bn[fm] column fm.
+    auto row = [&](f32x4(&acc)[FM][FN], bf16x8(&af)[FM], const bf16x8(&bc)[FN], int fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bc[fn], acc[fm][fn], 0,
+                                                                  0, 0);
+    };
+    auto kstep = [&](f32x4(&acc)[FM][FN], bf16x8(&af)[FM], const bf16x8(&bc)[FN],
+                     bf16x8(&bn)[FN], const uint8_t* st_n, int ks_n) {
+        // rows with a B column read beside the A row (WT: 2 reads, else 3
+        // with the two transposed halves), then rows with the A read only;
+        // each row's MFMAs are issued before its reads
+#pragma unroll
+        for (int fm = 0; fm < FN; ++fm) {
+            row(acc, af, bc, fm);
+            af[fm] = read_a(st_n, ks_n, fm);
+            bn[fm] = read_b(st_n, ks_n, fm);
+            __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, WT ? 2 : 3, 0);
+        }
+#pragma unroll
+        for (int fm = FN; fm < FM; ++fm) {
+            row(acc, af, bc, fm);
+            af[fm] = read_a(st_n, ks_n, fm);
+            __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    ParkOut<T> po;
+    po.rs = __builtin_amdgcn_make_buffer_rsrc(g.Y + (size_t)row0 * g.ldy + col0, 0, 0x7fffffff,
+                                              RAW_BUFFER_FLAGS);
+    po.full = (row0 + BM <= g.M) && (col0 + BN <= g.N);
+    po.ld = (int)g.ldy;
+    po.rows_left = g.M - row0;
+    po.cols_left = g.N - col0;
+    po.wave = wave;
+    po.wrow = wm * TM;
+    po.wcol = wn * TN;
+
+    // acc: the MFMA target of every chunk; keep0, keep1: the saved subtree
+    // levels below the parked one
+    f32x4 acc[FM][FN], keep0[FM][FN], keep1[FM][FN];
+#pragma unroll
+    for (int p = 0; p < STAGES; ++p)
+        if (p < total)
+            issue(p);
+    if (STAGES - 1 < total)
+        wait_vmcnt<(STAGES - 1) * LOADS_PER_ISSUE>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Every wave runs its MFMAs, also one whose rows or columns lie wholly
+    // past M or N (edge tiles): its operands read as zeros and its results
+    // are dropped by the stores' range checks, and the loop has no branch.
+    bf16x8 af[FM], b0[FN], b1[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+        af[fm] = read_a(smem, 0, fm);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        b0[fn] = read_b(smem, 0, fn);
+
+    auto zero = [&](f32x4(&v)[FM][FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                v[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // acc = left + acc, element by element (the node's left operand first)
+    auto add_left = [&](const f32x4(&left)[FM][FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = left[fm][fn] + acc[fm][fn];
+    };
+    auto keep = [&](f32x4(&dst)[FM][FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                dst[fm][fn] = acc[fm][fn];
+    };
+
+    // chunk c into acc: its MFMA chain from +0 over the chunk's K blocks
+    // (every block holds two k steps: Kc % 64 == 0 on this tile)
+    auto chunk = [&](int c) {
+        zero(acc);
+        for (int b = 0; b < nb; ++b) {
+            const int t = c * nb + b;
+            const uint8_t* st = smem + (t % STAGES) * STAGE_BYTES;
+            const uint8_t* st_next = smem + ((t + 1) % STAGES) * STAGE_BYTES;
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(acc, af, b0, b1, st, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkmcnt0();
+            if (t + STAGES - 1 < total)
+                wait_vmcnt<(STAGES - 2) * LOADS_PER_ISSUE>();
+            else
+                wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + STAGES < total)
+                issue(t + STAGES);
+            __builtin_amdgcn_sched_barrier(0);
+            // the next block's reads are harmless after the last block
+            kstep(acc, af, b1, b0, st_next, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    chunk(0);
+    keep(keep0);                     // c0
+    chunk(1);
+    add_left(keep0);                 // c0 + c1
+    keep(keep1);
+    chunk(2);
+    keep(keep0);                     // c2
+    chunk(3);
+    add_left(keep0);                 // c2 + c3
+    add_left(keep1);                 // (c0 + c1) + (c2 + c3)
+    __builtin_amdgcn_sched_barrier(0);
+    park_out_store<T>(po, acc, lane);
+    chunk(4);
+    keep(keep0);                     // c4
+    chunk(5);
+    add_left(keep0);                 // c4 + c5
+    keep(keep1);
+    chunk(6);
+    keep(keep0);                     // c6
+    chunk(7);
+    // chunk 7
+    add_left(keep0);                 // c6 + c7
+    add_left(keep1);                 // (c4 + c5) + (c6 + c7)
+    __builtin_amdgcn_sched_barrier(0);
+    park_out_add<T>(po, acc, lane);  // the left half + the right half
+
+    // the final product through the stage buffers (addmm epilogue on the way)
+    store_tile_via_lds<T, STAGES>(acc, g, g.Y, (int)g.ldy, row0, col0, wm, wn, lane, tid, smem);
+}
+
+template <bool WT>
+hipError_t launch_wide(const GemmArgs& g, hipStream_t s)
+{
+    constexpr int ST = 3;
+    auto fn = wide_gemm_kernel<TileW, ST, WT>;
+    constexpr int bytes = ST * TileW::STAGE_BYTES;
+    static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
+    static std::atomic<unsigned long long> lds_set{0};
+    const hipError_t attr = ensure_lds_limit(lds_set, reinterpret_cast<const void*>(fn), bytes);
+    if (attr != hipSuccess)
+        return attr;
+    const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * g.slices);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(TileW::THREADS), bytes, s, g);
+    return hipGetLastError();
 }
 
 // Stage counts.  With 8 chunks per slice the top subtree level is parked in
@@ -689,6 +1078,13 @@ hipError_t launch_layout(int tile, const GemmArgs& g, int cps, hipStream_t s)
         if constexpr (EPI == EPI_STORE)
             return g.wt ? launch<Tile256, 1, EPI, true>(g, s) : launch<Tile256, 1, EPI, false>(g, s);
     }
+    if (tile == TILE_W256) {
+        // eight-chunk workgroups writing the final product only
+        if (cps != 8 || EPI != EPI_STORE)
+            return hipErrorInvalidValue;
+        if constexpr (EPI == EPI_STORE)
+            return g.wt ? launch_wide<true>(g, s) : launch_wide<false>(g, s);
+    }
     if (tile == TILE_D64)
         return g.wt ? launch_cps<TileD64, TileD64, EPI, true>(g, cps, s)
                     : launch_cps<TileD64, TileD64, EPI, false>(g, cps, s);
@@ -704,13 +1100,21 @@ bool lds_engine_supports(int tile, const GemmArgs& g, int cps)
     // every MFMA step inside K, and byte offsets of the tile's X rows, W
     // columns and output rows within the 31-bit record range of a buffer
     // descriptor; the 256x256 tile for one-chunk slices only
-    if (g.Kc % 32 != 0 || (tile != TILE_L128 && tile != TILE_L256 && tile != TILE_D64))
+    if (g.Kc % 32 != 0 ||
+        (tile != TILE_L128 && tile != TILE_L256 && tile != TILE_D64 && tile != TILE_W256))
         return false;
     if (tile == TILE_L256 && cps != 1)
         return false;
+    // the output-parked tile: eight chunks, a final fp32 output that the
+    // park may use (not slice roots, not bf16)
+    if (tile == TILE_W256 &&
+        (cps != 8 || g.Kc % 64 != 0 || g.out_z_stride != 0 || (g.epi && g.out_bf16)))
+        return false;
     const size_t BM = tile == TILE_L256 ? lds::Tile256::BM
+                      : tile == TILE_W256 ? lds::TileW::BM
                       : tile == TILE_D64 ? lds::TileD64::BM : lds::Tile128::BM;
     const size_t BN = tile == TILE_L256 ? lds::Tile256::BN
+                      : tile == TILE_W256 ? lds::TileW::BN
                       : tile == TILE_D64 ? lds::TileD64::BN : lds::Tile128::BN;
     const size_t xbytes = ((BM - 1) * g.ldx + g.K) * 2;
     const size_t wbytes = g.wt ? ((BN - 1) * g.ldw + g.K) * 2 : ((size_t)g.K * g.ldw) * 2;

@@ -28,7 +28,7 @@ inline hipError_t ensure_lds_limit(std::atomic<unsigned long long>& done, const 
 }
 
 enum { EPI_STORE = 0, EPI_COMBINE = 1, EPI_ATOMIC = 2 };
-enum { TILE_S16 = 0, TILE_M64 = 1, TILE_L128 = 2, TILE_L256 = 3, TILE_D64 = 4 };
+enum { TILE_S16 = 0, TILE_M64 = 1, TILE_L128 = 2, TILE_L256 = 3, TILE_D64 = 4, TILE_W256 = 5 };
 
 struct GemmArgs {
     const uint16_t* X;
