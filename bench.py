@@ -1,31 +1,46 @@
 """Benchmark of the deterministic-reduction hot path on one MI355X.
 
-One step = one pass of every operation on the path over one batch of
-seeded synthetic input shaped like an 8B-class model (hidden 4096, MLP 14336,
-vocabulary 151936), batch 256:
-  rmsnorm      inv_rmsnorm           x[256,4096] bf16 -> fp32
-  shrink       det_splitk_gemm       X[256,4096] A[4096,64], 8 slices
-  shrink_atom  atomic_splitk_gemm    the same product, fp32 atomics (control)
-  cast         detred_f32_to_bf16    shrink output -> bf16
-  expand       det_splitk_gemm       [256,64] B[64,4096]
-  dense        det_splitk_gemm       X[256,4096] W[4096,14336]
-  tp_shards    tree_tp_shards_gemm   X[512,8192] W[8192,8192]: 8 virtual shards'
-                                     subtree roots (what each rank computes)
-  tp_combine   tree_combine_f32      the top 3 tree levels over the 8 roots
-                                     (what the cross-rank reduction computes)
-  log_softmax_mean inv_log_softmax_mean logits[256,151936] fp32: log_softmax
-                                     and the row mean in one pass over the
-                                     logits (the bits of inv_log_softmax and
-                                     inv_mean, which are checked against it)
-Every operation runs in libdetred's HIP kernels.  The step's three
-independent chains (dense -> log_softmax_mean; the tree-TP pair; rmsnorm,
-the LoRA shrink/control/cast/expand) run on three streams of default
-priority, forked from and joined to the main stream with events; the same
-ops issued serially on one stream are timed too (ms_per_step_serial).
-`value` is the deterministic GEMM work of a step (shrink, expand, dense,
-tree-TP) divided by the step time.  Each operation is also timed alone
-with HIP events on the stream it runs on; the slowest one gets the roofline
-object.
+Headline (the JSON line's `value`): deterministic split-K GEMM TFLOP/s on
+the largest single-GPU configuration, the batch-invariant dense product
+    det_splitk_gemm  Y[4096,14336] fp32 = X[4096,4096] W[4096,14336] bf16
+at the automatic split.  A step is one call; `roofline` is that call's
+kernel, timed live with HIP events around every launch on its stream.
+
+Also reported (each operation in libdetred's HIP kernels):
+  step_b256       one pass of every operation on the path over a batch of
+                  256 rows of an 8B-class layer (hidden 4096, MLP 14336,
+                  vocabulary 151936), three independent chains on three
+                  streams: rmsnorm; LoRA shrink X[256,4096] A[4096,64] at
+                  8 slices, rounded to bf16 in its own epilogue, with the
+                  atomic control beside it, then the expand; dense
+                  X[256,4096] W[4096,14336]; tree-TP X[512,8192]
+                  W[8192,8192] with 8 virtual shards (shard roots, then
+                  the cross-rank tree); log_softmax + mean over
+                  logits[256,151936] in one pass;
+  det_vs_atomic   per-call time of det split-K vs the atomic control at the
+                  same split vs unsplit, over the LoRA shrink grid (M in
+                  1, 8, 64, 256; r in 16, 64; split 4, 8), the 16x16x512
+                  shrink, the dense product (M in 1, 1024, 4096) and the
+                  tree-TP product: back-to-back calls between one event
+                  pair, and the same calls replayed from a HIP graph;
+  replay_divergence  100 identical-input replays of det and atomic over
+                  the LoRA shrink grid: the share of replays 1..99 that
+                  differ from replay 0, the distinct outputs among the 100,
+                  the mean share of differing elements;
+  configs         every configuration timed alone, warm and cold, against
+                  its roofline;
+  cpu_baseline    the oracle (fp64, all host cores) on row blocks of the
+                  headline product.
+
+Profiling modes (one operation at a time, for rocprofv3):
+  --profile-op NAME   warm-up, then --steps launches of one operation
+                      (dense_m1024, dense_m4096, tree_tp_t1, tree_tp_t8,
+                      rmsnorm_b4096, log_softmax_mean_b4096, step_b256);
+  --det-atomic-trace  the det_vs_atomic calls, each (setting, variant)
+                      block inside a roctx range named after it;
+  --summarize-trace DIR  kernel-only time per call of every block, from the
+                      kernel and marker traces rocprofv3 wrote in DIR (no
+                      GPU needed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -50,6 +65,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
+HEAD_M, HEAD_K, HEAD_N = 4096, 4096, 14336   # the headline product
+
 B = 256          # batch rows of the step
 H = 4096         # hidden size
 R = 64           # LoRA rank
@@ -57,9 +74,10 @@ F = 14336        # MLP width
 V = 151936       # vocabulary
 TP_M, TP_K, TP_N, TP_T = 512, 8192, 8192, 8
 
-WORKLOAD = ("hot_path_8b_b256: rmsnorm[256,4096]; lora shrink X[256,4096]A[4096,64] det split-K=8 "
-            "(+atomic control); bf16 cast; expand [256,64]B[64,4096]; dense X[256,4096]W[4096,14336]; "
-            "tree-TP X[512,8192]W[8192,8192] T=8; log_softmax+mean logits[256,151936] (one pass)")
+STEP_WORKLOAD = ("hot_path_8b_b256: rmsnorm[256,4096]; lora shrink X[256,4096]A[4096,64] det "
+                 "split-K=8 into bf16 (+atomic control); expand [256,64]B[64,4096]; dense "
+                 "X[256,4096]W[4096,14336]; tree-TP X[512,8192]W[8192,8192] T=8; log_softmax+mean "
+                 "logits[256,151936] (one pass)")
 
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -85,7 +103,6 @@ class Workload:
         self.Xt, self.Wt = d16(Xt, dev), d16(Wt, dev)
         self.lg = torch.from_numpy(lg).to(dev)
         self.y_rms = torch.empty((B, H), dtype=f32, device=dev)
-        self.y_shr = torch.empty((B, R), dtype=f32, device=dev)
         self.y_atm = torch.empty((B, R), dtype=f32, device=dev)
         self.y_b16 = torch.empty((B, R), dtype=torch.int16, device=dev)
         self.y_exp = torch.empty((B, H), dtype=f32, device=dev)
@@ -104,7 +121,7 @@ class Workload:
         and one [M,N] result).  Each launch re-issues a C call whose arguments were
         marshalled once, on streams[lane].  Lanes are independent chains:
         0 dense -> log_softmax_mean; 1 the tree-TP pair; 2 rmsnorm, the
-        LoRA shrink/control/cast/expand."""
+        LoRA shrink/control/expand."""
         gb = 2  # bytes per bf16
 
         def P(lane, fn, *args):
@@ -112,12 +129,13 @@ class Workload:
         return [
             ("rmsnorm", P(2, detred.inv_rmsnorm, self.x, self.g, self.y_rms, 1e-6),
              0, B * H * gb + H * gb + B * H * 4, 2),
-            ("shrink", P(2, detred.det_splitk_gemm, self.X, self.A, self.y_shr, 8, self.ws_shr),
-             2 * B * H * R, B * H * gb + H * R * gb + B * R * 4, 2),
+            # the shrink rounds its result to bf16 in its own epilogue (the
+            # bits of a separate cast, one launch fewer)
+            ("shrink", P(2, detred.det_splitk_addmm, self.X, self.A, self.y_b16, None, 1.0, 1.0,
+                         8, self.ws_shr),
+             2 * B * H * R, B * H * gb + H * R * gb + B * R * gb, 2),
             ("shrink_atom", P(2, detred.atomic_splitk_gemm, self.X, self.A, self.y_atm, 8),
              0, B * H * gb + H * R * gb + B * R * 4, 2),
-            ("cast", P(2, detred.detred_f32_to_bf16, self.y_shr, self.y_b16),
-             0, B * R * 4 + B * R * gb, 2),
             ("expand", P(2, detred.det_splitk_gemm, self.y_b16, self.B, self.y_exp, 0),
              2 * B * R * H, B * R * gb + R * H * gb + B * H * 4, 2),
             ("dense", P(0, detred.det_splitk_gemm, self.X, self.W, self.y_dns, 0, self.ws_dns),
@@ -221,31 +239,344 @@ def cold_time_us(fn, reps, stream, flush):
     return ts[len(ts) // 2]
 
 
-def latency_ratios(dev, stream):
-    """Deterministic split-K=8 vs atomic split-K=8 (zero fill included) vs
-    unsplit, on the LoRA shrink shapes; interleaved, medians of 200."""
+# -- deterministic vs atomic vs unsplit ------------------------------------
+
+def roctx():
+    """roctxRangePushA / roctxRangePop of the profiler SDK's marker library
+    (rocprofv3 --marker-trace records them), or None without it."""
+    import ctypes
+    for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+        try:
+            L = ctypes.CDLL(name)
+        except OSError:
+            continue
+        L.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        L.roctxRangePushA.restype = ctypes.c_int
+        L.roctxRangePop.restype = ctypes.c_int
+        return L
+    return None
+
+
+def det_atomic_settings():
+    """(name, variants, calls per timing) for every det-vs-atomic setting:
+    variants maps det / atomic / unsplit to (fn, *args) with the split
+    fixed; all buffers are drawn once here."""
+    sets = []
+    for (M, K, r, S) in ([(16, 512, 16, 8)] +
+                         [(M, 4096, r, S) for S in (4, 8) for r in (16, 64)
+                          for M in (1, 8, 64, 256)]):
+        X, A, _ = inputs.lora_inputs(M, K, r, 0)
+        sets.append(("shrink_%dx%dx%d_s%d" % (M, r, K, S), "gemm", (M, r, K, S), X, A, 200))
+    for M in (1, 1024, 4096):
+        X, W = inputs.dense_inputs(M, 4096, 14336, 0)
+        S = detred.auto_split(M, 14336, 4096)
+        sets.append(("dense_%dx14336x4096_s%d" % (M, S), "gemm", (M, 14336, 4096, S), X, W,
+                     200 if M == 1 else 20))
+        if S != 8:
+            sets.append(("dense_%dx14336x4096_s8" % M, "gemm", (M, 14336, 4096, 8), X, W,
+                         200 if M == 1 else 20))
+    X, W = inputs.dense_inputs(TP_M, TP_K, TP_N, 0)
+    sets.append(("tree_tp_512x8192x8192_t8", "tp", (TP_M, TP_N, TP_K, 8), X, W, 50))
+    return sets
+
+
+def det_atomic_calls(kind, dims, X, W, dev):
+    """Prepared calls of one setting: det (split S, or T shards), atomic at
+    the same split, unsplit (det at split 1)."""
+    M, N, K, S = dims
+    Xd, Wd = d16(X, dev), d16(W, dev)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    Ya = torch.empty_like(Y)
+    Y1 = torch.empty_like(Y)
+    ws = detred.workspace(M, N, K, S, dev)
+    det_fn = detred.tree_tp_gemm if kind == "tp" else detred.det_splitk_gemm
+    return {"det": detred.prepare(det_fn, Xd, Wd, Y, S, ws),
+            "atomic": detred.prepare(detred.atomic_splitk_gemm, Xd, Wd, Ya, S),
+            "unsplit": detred.prepare(detred.det_splitk_gemm, Xd, Wd, Y1, 1)}
+
+
+def back_to_back_us(fn, calls, stream):
+    """Per-call time of `calls` back-to-back launches between one event
+    pair (after a burst of warm-up calls, so the queue is full and the GPU
+    runs them without host gaps)."""
+    for _ in range(min(calls, 20)):
+        fn()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(calls):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1000.0 / calls
+
+
+def graph_us(make, calls, dev):
+    """Per-call time of `calls` launches captured in one HIP graph and
+    replayed (no host launch gaps at all; the inter-kernel gaps of the
+    GPU's own dispatch remain).  `make` prepares the call on the capture
+    stream."""
+    side = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(side):
+        fn = make()
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn = make()
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    t0.record(st)
+    g.replay()
+    t1.record(st)
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) * 1000.0 / calls
+
+
+def det_vs_atomic(dev, stream):
+    """Per-call microseconds of det, the atomic control (its zero fill
+    included) and unsplit on every setting, interleaved over three rounds
+    (medians), back to back and from a HIP graph; with the det/atomic and
+    det/unsplit ratios of both."""
     out = {}
-    for (M, K, r) in [(16, 512, 16), (256, 4096, 64), (256, 4096, 16), (1, 4096, 64)]:
+    for (name, kind, dims, X, W, calls) in det_atomic_settings():
+        fns = det_atomic_calls(kind, dims, X, W, dev)
+        eager = {k: [] for k in fns}
+        for _ in range(3):
+            for k, fn in fns.items():
+                eager[k].append(back_to_back_us(fn, calls, stream))
+        e = {k: statistics.median(v) for k, v in eager.items()}
+        gr = {}
+        M, N, K, S = dims
+        Xd, Wd = d16(X, dev), d16(W, dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = detred.workspace(M, N, K, S, dev)
+        det_fn = detred.tree_tp_gemm if kind == "tp" else detred.det_splitk_gemm
+        makers = {"det": lambda: detred.prepare(det_fn, Xd, Wd, Y, S, ws),
+                  "atomic": lambda: detred.prepare(detred.atomic_splitk_gemm, Xd, Wd, Y, S),
+                  "unsplit": lambda: detred.prepare(detred.det_splitk_gemm, Xd, Wd, Y, 1)}
+        for k, mk in makers.items():
+            gr[k] = graph_us(mk, calls, dev)
+        out[name] = {
+            "det_us": round(e["det"], 2), "atomic_us": round(e["atomic"], 2),
+            "unsplit_us": round(e["unsplit"], 2),
+            "det_over_atomic": round(e["det"] / e["atomic"], 4),
+            "det_over_unsplit": round(e["det"] / e["unsplit"], 4),
+            "graph_det_us": round(gr["det"], 2), "graph_atomic_us": round(gr["atomic"], 2),
+            "graph_unsplit_us": round(gr["unsplit"], 2),
+            "graph_det_over_atomic": round(gr["det"] / gr["atomic"], 4),
+        }
+        del fns, Y, ws
+    return out
+
+
+def det_atomic_trace(dev, stream):
+    """The det_vs_atomic calls for a kernel trace: every (setting, variant)
+    block of launches runs inside a roctx range 'detatom:<setting>:<variant>:<calls>'
+    and ends with a synchronisation, so each kernel of the trace belongs to
+    the range it starts in."""
+    L = roctx()
+    if L is None:
+        print("bench: no roctx library; the trace will have no ranges", file=sys.stderr)
+    for (name, kind, dims, X, W, calls) in det_atomic_settings():
+        fns = det_atomic_calls(kind, dims, X, W, dev)
+        for k, fn in fns.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            if L is not None:
+                L.roctxRangePushA(("detatom:%s:%s:%d" % (name, k, calls)).encode())
+            for _ in range(calls):
+                fn()
+            torch.cuda.synchronize()
+            if L is not None:
+                L.roctxRangePop()
+        del fns
+    print("bench: det/atomic trace done", file=sys.stderr, flush=True)
+
+
+def read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(d):
+    """Kernel-only time per call of every det/atomic block, from the
+    kernel trace and the marker trace rocprofv3 wrote under directory d
+    (any *kernel_trace.csv and *marker_api_trace.csv below it).  Prints a
+    markdown table; no GPU needed."""
+    import glob
+    kt = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    mt = sorted(glob.glob(os.path.join(d, "**", "*marker_api_trace.csv"), recursive=True))
+    if not kt or not mt:
+        sys.exit("summarize: no kernel_trace.csv / marker_api_trace.csv under %s" % d)
+    kernels = read_csv(kt[0])
+    ranges = []
+    for row in read_csv(mt[0]):
+        text = next((v for v in row.values() if isinstance(v, str) and v.startswith("detatom:")),
+                    None)
+        if text is None:
+            continue
+        _, setting, variant, calls = text.split(":")
+        ranges.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]), setting, variant,
+                       int(calls)))
+    ranges.sort()
+    per = {}
+    for k in kernels:
+        st, en = int(k["Start_Timestamp"]), int(k["End_Timestamp"])
+        for (a, b, setting, variant, calls) in ranges:
+            if a <= st <= b:
+                e = per.setdefault((setting, variant), [0, 0, calls, set()])
+                e[0] += en - st
+                e[1] += 1
+                e[3].add(k["Kernel_Name"].split("(")[0][:60])
+                break
+    rows = {}
+    for (setting, variant), (ns, n, calls, names) in per.items():
+        rows.setdefault(setting, {})[variant] = (ns / 1000.0 / calls, n / calls, names)
+    print("| setting | det us | atomic us | unsplit us | det/atomic | det/unsplit | "
+          "kernels per call (det / atomic / unsplit) |")
+    print("|---|---|---|---|---|---|---|")
+    for setting in sorted(rows, key=lambda x: (x.split("_")[0], len(x), x)):
+        r = rows[setting]
+        if not all(v in r for v in ("det", "atomic", "unsplit")):
+            continue
+        d_, a_, u_ = r["det"][0], r["atomic"][0], r["unsplit"][0]
+        print("| %s | %.2f | %.2f | %.2f | %.3f | %.3f | %.0f / %.0f / %.0f |" % (
+            setting, d_, a_, u_, d_ / a_, d_ / u_, r["det"][1], r["atomic"][1], r["unsplit"][1]))
+
+
+def short_kernel(name):
+    """A kernel's name without its argument list and namespaces."""
+    n = name.split("(")[0]
+    for pre in ("void ", "detred::lds::", "detred::"):
+        n = n.replace(pre, "")
+    return n[:90]
+
+
+def summarize_profile(d):
+    """Per (kernel, grid) figures from the rocprofv3 CSVs under directory d:
+    dispatch count and average / min / max duration from a kernel trace,
+    the per-dispatch mean of every counter from a counter collection.
+    Prints markdown; no GPU needed."""
+    import glob
+    for kt in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        agg = {}
+        for k in read_csv(kt):
+            key = (short_kernel(k["Kernel_Name"]), k.get("Grid_Size_X") or k.get("Grid_Size", ""))
+            agg.setdefault(key, []).append((int(k["End_Timestamp"]) - int(k["Start_Timestamp"])) / 1e3)
+        print("Kernel trace `%s`\n" % os.path.relpath(kt, d))
+        print("| kernel | grid | dispatches | avg us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for (name, grid), ts in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            print("| `%s` | %s | %d | %.2f | %.2f | %.2f |" % (name, grid, len(ts), sum(ts) / len(ts),
+                                                          min(ts), max(ts)))
+        print()
+    for cc in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        vals = {}
+        counters = []
+        for r in read_csv(cc):
+            key = (short_kernel(r["Kernel_Name"]), r.get("Grid_Size", ""))
+            c = r["Counter_Name"]
+            if c not in counters:
+                counters.append(c)
+            vals.setdefault(key, {}).setdefault(c, {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[key][c][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        print("Counters `%s` (per-dispatch means)\n" % os.path.relpath(cc, d))
+        print("| kernel | grid | dispatches | " + " | ".join(counters) + " |")
+        print("|---|---|---|" + "---|" * len(counters))
+        for (name, grid), cv in sorted(vals.items()):
+            n = max(len(v) for v in cv.values())
+            cells = ["%.6g" % (sum(cv[c].values()) / len(cv[c])) if c in cv else "-" for c in counters]
+            print("| `%s` | %s | %d | %s |" % (name, grid, n, " | ".join(cells)))
+        print()
+
+
+LIB_KERNELS = ("gemm_kernel", "tree_combine", "rmsnorm", "log_softmax", "mean_kernel",
+               "fill_zero", "cast_bf16", "attention", "epilogue_only")
+
+
+def write_traffic(fetch_dir, write_dir, calls):
+    """profiles/traffic.json from two counter runs per operation (FETCH_SIZE
+    under fetch_dir/<op>/, WRITE_SIZE under write_dir/<op>/, each run
+    preceded by a 256 MiB device-to-device copy): HBM bytes per call of the
+    operation = the library kernels' FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the copy,
+    summed over the run's dispatches and divided by its `calls`."""
+    import glob
+    copy_bytes = 256 << 20
+
+    def per_op(root, counter):
+        out, scale = {}, None
+        for op in sorted(os.listdir(root)):
+            files = glob.glob(os.path.join(root, op, "**", "*counter_collection.csv"), recursive=True)
+            if not files:
+                continue
+            lib_kib, copy_kib = 0.0, []
+            for r in read_csv(files[0]):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if "copyBuffer" in r["Kernel_Name"]:
+                    copy_kib.append(v)
+                elif any(t in r["Kernel_Name"] for t in LIB_KERNELS):
+                    lib_kib += v
+            if copy_kib and scale is None:
+                scale = copy_bytes / (max(copy_kib) * 1024.0)
+            out[op] = lib_kib
+        return out, scale
+    fetch, fs = per_op(fetch_dir, "FETCH_SIZE")
+    write, ws = per_op(write_dir, "WRITE_SIZE")
+    ops = {op: int(round((fetch[op] * fs + write.get(op, 0.0) * ws) * 1024.0 / calls))
+           for op in fetch}
+    raw = {op: [round(fetch[op] / calls, 1), round(write.get(op, 0.0) / calls, 1)] for op in fetch}
+    print(json.dumps({"source_hash": source_hash(),
+                      "workload": "bench.py --profile-op <op> --steps S --warmup W "
+                                  "--copy-calibration, %d calls per op" % calls,
+                      "calibration": "a 256 MiB device-to-device copy; scale factors fetch x%.4f, "
+                                     "write x%.4f" % (fs, ws),
+                      "scale_fetch": round(fs, 4), "scale_write": round(ws, 4), "ops": ops,
+                      "raw_kib_per_call": raw}, indent=1))
+
+
+# -- replay divergence ------------------------------------------------------
+
+def divergence(dev):
+    """Replay divergence of det vs the atomic control over 100 identical-
+    input replays on the LoRA shrink grid (M in 1, 8, 64, 256; r in 16, 64;
+    split 4 and 8) and the 16x16x512 shrink: the share of replays 1..99
+    that differ anywhere from replay 0, the number of distinct outputs among
+    the 100, and the mean share of elements that differ from replay 0."""
+    out = {}
+    grid = [(16, 512, 16, 8)] + [(M, 4096, r, S) for S in (4, 8) for r in (16, 64)
+                                  for M in (1, 8, 64, 256)]
+    for (M, K, r, S) in grid:
         X, A, _ = inputs.lora_inputs(M, K, r, 0)
         Xd, Ad = d16(X, dev), d16(A, dev)
         Y = torch.empty((M, r), dtype=torch.float32, device=dev)
-        ws = detred.workspace(M, r, K, 8, dev)
-        fns = {
-            "det8": detred.prepare(detred.det_splitk_gemm, Xd, Ad, Y, 8, ws),
-            "atomic8": detred.prepare(detred.atomic_splitk_gemm, Xd, Ad, Y, 8),
-            "unsplit": detred.prepare(detred.det_splitk_gemm, Xd, Ad, Y, 1),
-        }
-        med = {k: [] for k in fns}
-        for _ in range(3):  # interleave the variants
-            for k, fn in fns.items():
-                med[k].append(median_time_us(fn, 200, stream)[0])
-        m = {k: statistics.median(v) for k, v in med.items()}
-        out["%dx%dx%d" % (M, r, K)] = {
-            "det8_us": round(m["det8"], 2), "atomic8_us": round(m["atomic8"], 2),
-            "unsplit_us": round(m["unsplit"], 2),
-            "det_over_atomic": round(m["det8"] / m["atomic8"], 4),
-            "det_over_unsplit": round(m["det8"] / m["unsplit"], 4),
-        }
+        ws = detred.workspace(M, r, K, S, dev)
+        res = {}
+        for name, fn in (("det", detred.prepare(detred.det_splitk_gemm, Xd, Ad, Y, S, ws)),
+                         ("atomic", detred.prepare(detred.atomic_splitk_gemm, Xd, Ad, Y, S))):
+            outs = []
+            for _ in range(100):
+                fn()
+                outs.append(Y.view(torch.int32).clone())
+            torch.cuda.synchronize()
+            ref = outs[0]
+            differ = [int((o != ref).sum()) for o in outs[1:]]
+            hashes = {hashlib.sha256(o.cpu().numpy().tobytes()).hexdigest() for o in outs}
+            res[name] = [round(100.0 * sum(d > 0 for d in differ) / 99, 2), len(hashes),
+                         round(100.0 * sum(differ) / 99 / ref.numel(), 3)]
+        out["%dx%dx%d_s%d" % (M, r, K, S)] = res
     return out
 
 
@@ -264,18 +595,20 @@ def invariance(wl, dev):
         same += int(eq.sum())
         total += eq.numel()
 
-    f32 = torch.float32
-    # shrink: split 8 (step) vs unsplit, prefixes and single rows
-    ref = torch.empty((B, R), dtype=f32, device=dev)
-    detred.det_splitk_gemm(wl.X, wl.A, ref, 1)
-    cmp(wl.y_shr, ref)
+    f32, b16 = torch.float32, torch.int16
+    # shrink (bf16 output): split 8 (step) vs unsplit, prefixes and single rows
+    ref = torch.empty((B, R), dtype=b16, device=dev)
+    detred.det_splitk_addmm(wl.X, wl.A, ref, None, 1.0, 1.0, 1)
+    cmp(wl.y_b16, ref)
     for M in (1, 17, 128, 255):
-        y = torch.empty((M, R), dtype=f32, device=dev)
-        detred.det_splitk_gemm(wl.X[:M], wl.A, y, 8, detred.workspace(M, R, H, 8, dev))
+        y = torch.empty((M, R), dtype=b16, device=dev)
+        detred.det_splitk_addmm(wl.X[:M], wl.A, y, None, 1.0, 1.0, 8,
+                                detred.workspace(M, R, H, 8, dev))
         cmp(y, ref[:M])
     for j in (5, 200):
-        y = torch.empty((1, R), dtype=f32, device=dev)
-        detred.det_splitk_gemm(wl.X[j:j + 1], wl.A, y, 8, detred.workspace(1, R, H, 8, dev))
+        y = torch.empty((1, R), dtype=b16, device=dev)
+        detred.det_splitk_addmm(wl.X[j:j + 1], wl.A, y, None, 1.0, 1.0, 8,
+                                detred.workspace(1, R, H, 8, dev))
         cmp(y, ref[j:j + 1])
     # dense: prefixes, split 4 vs policy
     for M in (1, 16, 128):
@@ -323,35 +656,6 @@ def tp_breakdown(wl, dev, stream):
     y = torch.empty((TP_M, TP_N), dtype=torch.float32, device=dev)
     out["combine_T8_us"] = round(median_time_us(
         detred.prepare(detred.tree_combine_f32, P, y), 20, stream, warm=3)[0], 1)
-    return out
-
-
-def divergence(dev, stream):
-    """Replay divergence of det vs atomic split-K=8 over 100 replays on the
-    LoRA shrink shapes: the share of replays 1..99 that differ anywhere from
-    replay 0, the number of distinct outputs among the 100, and the mean
-    fraction of elements that differ from replay 0."""
-    out = {}
-    for (M, K, r) in [(16, 512, 16), (256, 4096, 64)]:
-        X, A, _ = inputs.lora_inputs(M, K, r, 0)
-        Xd, Ad = d16(X, dev), d16(A, dev)
-        Y = torch.empty((M, r), dtype=torch.float32, device=dev)
-        ws = detred.workspace(M, r, K, 8, dev)
-        res = {}
-        for name, fn in (("det8", detred.prepare(detred.det_splitk_gemm, Xd, Ad, Y, 8, ws)),
-                         ("atomic8", detred.prepare(detred.atomic_splitk_gemm, Xd, Ad, Y, 8))):
-            outs = []
-            for _ in range(100):
-                fn()
-                outs.append(Y.view(torch.int32).clone())
-            torch.cuda.synchronize()
-            ref = outs[0]
-            differ = [int((o != ref).sum()) for o in outs[1:]]
-            hashes = {hashlib.sha256(o.cpu().numpy().tobytes()).hexdigest() for o in outs}
-            res[name] = {"replays_differing_pct": round(100.0 * sum(d > 0 for d in differ) / 99, 2),
-                         "distinct_outputs": len(hashes),
-                         "mean_elements_differing_pct": round(100.0 * sum(differ) / 99 / ref.numel(), 3)}
-        out["%dx%dx%d" % (M, r, K)] = res
     return out
 
 
@@ -551,32 +855,151 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The oracle as it stands, on the host cores: one full step of the same
-    workload (every row of every operation), repeated until min_seconds."""
+def cpu_baseline(X, W, min_seconds=10.0):
+    """The oracle as it stands, on the host cores: row blocks of 256 rows of
+    the headline product X W (fp64, every element of each block), block
+    after block until min_seconds have passed."""
     import oracle
-    h = wl.host
+    M = X.shape[0]
+    rows = 256
     flops = 0
-    reps = 0
+    blocks = 0
     t0 = time.perf_counter()
     while True:
-        oracle.rmsnorm(h["x"], h["g"], 1e-6)
-        y, _ = oracle.gemm(h["X"], h["A"], with_magnitude=False)
-        yb = oracle.f32_to_bf16(y.astype(np.float32))
-        oracle.gemm(yb, h["B"], with_magnitude=False)
-        oracle.gemm(h["X"], h["W"], with_magnitude=False)
-        oracle.gemm(h["Xt"], h["Wt"], with_magnitude=False)
-        oracle.log_softmax(h["lg"])
-        oracle.mean(h["lg"])
-        flops += 2 * B * H * R * 2 + 2 * B * H * F + 2 * TP_M * TP_K * TP_N
-        reps += 1
+        r0 = (blocks * rows) % M
+        oracle.gemm(X[r0:r0 + rows], W, with_magnitude=False)
+        flops += 2 * rows * X.shape[1] * W.shape[1]
+        blocks += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu": cpu_model(),
-            "sample": "%d full step(s) of the same workload in fp64 (all rows of shrink, expand, "
-                      "dense, tree-TP, rmsnorm, log_softmax, mean); %.1f s" % (reps, dt)}
+            "sample": "%d row block(s) of 256 x %d x %d of the headline product in fp64 "
+                      "(every element of each block); %.1f s" % (blocks, X.shape[1], W.shape[1],
+                                                                 dt)}
+
+
+class Headline:
+    """The headline call: det_splitk_gemm on X[4096,4096] W[4096,14336] at
+    the automatic split, inputs and output resident in HBM."""
+
+    def __init__(self, dev):
+        self.X, self.W = inputs.dense_inputs(HEAD_M, HEAD_K, HEAD_N, 0)
+        self.Xd, self.Wd = d16(self.X, dev), d16(self.W, dev)
+        self.Y = torch.empty((HEAD_M, HEAD_N), dtype=torch.float32, device=dev)
+        self.S = detred.auto_split(HEAD_M, HEAD_N, HEAD_K)
+        self.ws = detred.workspace(HEAD_M, HEAD_N, HEAD_K, 0, dev)
+        self.call = detred.prepare(detred.det_splitk_gemm, self.Xd, self.Wd, self.Y, 0, self.ws)
+        self.flops = 2 * HEAD_M * HEAD_K * HEAD_N
+        self.bytes = HEAD_M * HEAD_K * 2 + HEAD_K * HEAD_N * 2 + HEAD_M * HEAD_N * 4
+        self.workload = ("dense_4096x4096x14336: det_splitk_gemm Y[4096,14336] fp32 = "
+                         "X[4096,4096] W[4096,14336] bf16, automatic split (%d slice%s); the "
+                         "largest single-GPU configuration of the batch-invariant dense product"
+                         % (self.S, "" if self.S == 1 else "s"))
+
+
+def profile_op(name, dev, stream, steps, warmup):
+    """Warm-up, then `steps` launches of one operation (for rocprofv3)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def bf(shape, std):
+        return (torch.randn(shape, device=dev, generator=gen) * std).to(torch.bfloat16)
+    if name.startswith("dense_m"):
+        M = int(name[len("dense_m"):])
+        X, W = bf((M, HEAD_K), 1.0), bf((HEAD_K, HEAD_N), 0.02)
+        Y = torch.empty((M, HEAD_N), dtype=torch.float32, device=dev)
+        fn = detred.prepare(detred.det_splitk_gemm, X, W, Y, 0,
+                            detred.workspace(M, HEAD_N, HEAD_K, 0, dev))
+    elif name.startswith("tree_tp_t"):
+        T = int(name[len("tree_tp_t"):])
+        X, W = bf((TP_M, TP_K), 1.0), bf((TP_K, TP_N), 0.02)
+        Y = torch.empty((TP_M, TP_N), dtype=torch.float32, device=dev)
+        fn = detred.prepare(detred.tree_tp_gemm, X, W, Y, T,
+                            detred.workspace(TP_M, TP_N, TP_K, T, dev))
+    elif name == "rmsnorm_b4096":
+        x = bf((4096, H), 1.0)
+        g = (1.0 + 0.1 * torch.randn((H,), device=dev, generator=gen)).to(torch.bfloat16)
+        y = torch.empty((4096, H), dtype=torch.float32, device=dev)
+        fn = detred.prepare(detred.inv_rmsnorm, x, g, y, 1e-6)
+    elif name == "log_softmax_mean_b4096":
+        lg = torch.randn((4096, V), device=dev, generator=gen) * 3.0
+        ys = torch.empty_like(lg)
+        ym = torch.empty((4096,), dtype=torch.float32, device=dev)
+        fn = detred.prepare(detred.inv_log_softmax_mean, lg, ys, ym)
+    elif name == "step_b256":
+        wl = Workload(dev)
+        fn = Step(wl.ops([stream] * 3), [stream])
+    else:
+        sys.exit("unknown --profile-op %s" % name)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    print("bench: %d launches of %s done" % (steps, name), file=sys.stderr, flush=True)
+
+
+def step_b256(dev, stream, steps, warmup, quick):
+    """The B = 256 pass over every operation: whole-step time on three
+    streams and serially, per-op times, the bit-invariance share of its
+    rows, the tree-TP breakdown and its replay identity."""
+    wl = Workload(dev)
+    lanes = [stream, torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    ops = wl.ops(lanes)
+    serial_ops = wl.ops([stream, stream, stream])
+    step = Step(ops, lanes)
+    serial = Step(serial_ops, [stream])
+    for _ in range(warmup):
+        step()
+        serial()
+    torch.cuda.synchronize()
+    ms = time_steps(step, steps, stream) / steps
+    ms_serial = time_steps(serial, steps, stream) / steps
+    per_op = time_ops(serial_ops, steps, stream)
+    det_flops = sum(op[2] for op in ops)
+    op_stats = {}
+    for (name, _, fl, by, _), ts in zip(ops, per_op):
+        avg = sum(ts) / len(ts)
+        srt = sorted(ts)
+        st = {"avg_us": round(avg * 1000, 2), "median_us": round(statistics.median(ts) * 1000, 2),
+              "p10_us": round(srt[len(srt) // 10] * 1000, 2),
+              "p90_us": round(srt[(9 * len(srt)) // 10] * 1000, 2)}
+        if fl:
+            st["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
+        st["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
+        op_stats[name] = st
+    out = {"workload": STEP_WORKLOAD, "ms_per_step": round(ms, 4),
+           "ms_per_step_serial": round(ms_serial, 4),
+           "det_gemm_tflops": round(det_flops / (ms * 1e-3) / 1e12, 2),
+           "launches_lora_lane": 4, "ops": op_stats}
+    if quick:
+        return out
+    same, total = invariance(wl, dev)
+    out["bit_invariant_rows_pct"] = round(100.0 * same / max(total, 1), 4)
+    out["bit_invariant_rows_checked"] = total
+    out["tree_tp_breakdown"] = tp_breakdown(wl, dev, stream)
+    # replays: every deterministic output reproduced bit for bit; the
+    # atomic control counted
+    keys = ("y_b16", "y_dns", "y_tp", "y_lsm", "y_mean", "y_rms")
+    ref = {k: getattr(wl, k).clone() for k in keys}
+    atom0 = None
+    det_same = atom_diff = 0
+    for _ in range(20):
+        step()
+        torch.cuda.synchronize()
+        det_same += all(torch.equal(getattr(wl, k).view(torch.int32), v.view(torch.int32))
+                        for k, v in ref.items())
+        a = wl.y_atm.clone()
+        if atom0 is None:
+            atom0 = a
+        else:
+            atom_diff += not torch.equal(a.view(torch.int32), atom0.view(torch.int32))
+    out["det_replays_identical"] = "%d/20" % det_same
+    out["atomic_replays_differing"] = "%d/19" % atom_diff
+    return out
 
 
 def main():
@@ -586,14 +1009,31 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true",
-                    help="only the timed steps (for profiler runs): no ratios, "
-                         "invariance checks, breakdown or CPU baseline")
-    ap.add_argument("--serial", action="store_true",
-                    help="issue every op on the main stream (no overlap between kernels, "
-                         "so a profiler's per-kernel durations match the per-op timings)")
+                    help="only the headline and the B = 256 step's timings (for profiler runs)")
+    ap.add_argument("--profile-op", default=None,
+                    help="run --steps launches of one operation and exit (for rocprofv3)")
+    ap.add_argument("--det-atomic-trace", action="store_true",
+                    help="run the det/atomic/unsplit blocks inside roctx ranges and exit")
+    ap.add_argument("--summarize-trace", default=None,
+                    help="print kernel-only det/atomic times from a rocprofv3 output directory")
+    ap.add_argument("--summarize-profile", default=None,
+                    help="print per-kernel durations and counters from a rocprofv3 output "
+                         "directory")
+    ap.add_argument("--write-traffic", nargs=3, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CALLS"),
+                    help="print traffic.json from per-operation FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (HBM counter calibration)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], int(args.write_traffic[2]))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -611,89 +1051,76 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.profile_op:
+        for name in args.profile_op.split(","):
+            profile_op(name, dev, stream, args.steps, args.warmup)
+        return
+    if args.det_atomic_trace:
+        det_atomic_trace(dev, stream)
+        return
 
     print("bench: generating inputs", file=sys.stderr, flush=True)
-    wl = Workload(dev)
-    # the step's three independent chains on three streams (default
-    # priority), and the same ops all on the main stream for the serial
-    # step and the per-op timings
-    lanes = [stream, torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
-    if args.serial:
-        lanes = [stream]
-    ops = wl.ops(lanes * 3 if args.serial else lanes)
-    serial_ops = wl.ops([stream, stream, stream])
-    step = Step(ops, lanes)
-    serial = Step(serial_ops, [stream])
+    hd = Headline(dev)
     for _ in range(args.warmup):
-        step()
-        serial()
+        hd.call()
     torch.cuda.synchronize()
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-
-    total_ms = time_steps(step, args.steps, stream)
-    ms_per_step = total_ms / args.steps
-    ms_serial = time_steps(serial, args.steps, stream) / args.steps
-    per_op = time_ops(serial_ops, args.steps, stream)
-    det_flops = sum(op[2] for op in ops)
-    value = det_flops / (ms_per_step * 1e-3) / 1e12
-
-    op_stats = {}
-    for (name, _, fl, by, _), ts in zip(ops, per_op):
-        avg = sum(ts) / len(ts)
-        srt = sorted(ts)
-        st = {"avg_us": round(avg * 1000, 2), "median_us": round(statistics.median(ts) * 1000, 2),
-              "p10_us": round(srt[len(srt) // 10] * 1000, 2),
-              "p90_us": round(srt[(9 * len(srt)) // 10] * 1000, 2)}
-        if fl:
-            st["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
-        st["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
-        op_stats[name] = st
-    dom_i = max(range(len(ops)), key=lambda i: sum(per_op[i]))
-    dname, _, dfl, dby, _ = ops[dom_i]
-    davg_s = sum(per_op[dom_i]) / len(per_op[dom_i]) * 1e-3
-    if dfl and dfl / dby >= RIDGE:
-        roof = {"bound": "mfma", "achieved": round(dfl / davg_s / 1e12, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(dby / davg_s / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        hd.call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = hd.flops / (ms_per_step * 1e-3) / 1e12
+    # the kernel's own launches: an event pair around each, on its stream
+    launch = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(args.steps)]
+    for e0, e1 in launch:
+        e0.record(stream)
+        hd.call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    lt = sorted(e0.elapsed_time(e1) for e0, e1 in launch)
+    kavg_s = sum(lt) / len(lt) * 1e-3
+    roof = {"bound": "mfma", "achieved": round(hd.flops / kavg_s / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dname)
-    roof["kernel"] = dname
+    roof["traffic"] = measured_traffic("dense_m4096")
+    roof["kernel"] = ("det_splitk_gemm dense 4096x14336x4096, %d slice%s (%s launch%s per call)"
+                      % (hd.S, "" if hd.S == 1 else "s", "one" if hd.S == 1 else "two",
+                         "" if hd.S == 1 else "es"))
+    roof["launch_us"] = {"avg": round(kavg_s * 1e6, 2), "median": round(lt[len(lt) // 2] * 1e3, 2),
+                         "min": round(lt[0] * 1e3, 2), "max": round(lt[-1] * 1e3, 2)}
+    roof["algorithmic_bytes"] = hd.bytes
 
-    ratios = tp = div = ext = sweep = None
-    same = total = 0
+    print("bench: B = 256 step", file=sys.stderr, flush=True)
+    step = step_b256(dev, stream, min(args.steps, 20), min(args.warmup, 5), args.quick)
+
+    ratios = div = ext = sweep = None
     if not args.quick:
-        print("bench: latency ratios, invariance, tree-TP breakdown", file=sys.stderr, flush=True)
-        ratios = latency_ratios(dev, stream)
-        same, total = invariance(wl, dev)
-        tp = tp_breakdown(wl, dev, stream)
-        div = divergence(dev, stream)
+        print("bench: det vs atomic vs unsplit", file=sys.stderr, flush=True)
+        ratios = det_vs_atomic(dev, stream)
+        print("bench: replay divergence", file=sys.stderr, flush=True)
+        div = divergence(dev)
         print("bench: next-row operations", file=sys.stderr, flush=True)
         ext = extensions(dev, stream)
         print("bench: configuration sweep", file=sys.stderr, flush=True)
         sweep = config_sweep(dev, stream)
-
-    # replays: every deterministic output is reproduced bit for bit; the
-    # atomic control is counted
-    ref = {k: getattr(wl, k).clone() for k in ("y_shr", "y_dns", "y_tp", "y_lsm", "y_mean", "y_rms")}
-    atom0 = None
-    det_same = atom_diff = 0
-    for r in range(20):
-        step()
+    # the headline output is reproduced bit for bit
+    ref = hd.Y.clone()
+    same = 0
+    for _ in range(5):
+        hd.call()
         torch.cuda.synchronize()
-        det_same += all(torch.equal(getattr(wl, k).view(torch.int32), v.view(torch.int32))
-                        for k, v in ref.items())
-        a = wl.y_atm.clone()
-        if atom0 is None:
-            atom0 = a
-        else:
-            atom_diff += not torch.equal(a.view(torch.int32), atom0.view(torch.int32))
+        same += torch.equal(hd.Y.view(torch.int32), ref.view(torch.int32))
 
     cpu = None
     if not args.no_cpu_baseline and not args.quick:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl)
+        cpu = cpu_baseline(hd.X, hd.W)
 
     line = {
         "metric": "det split-K GEMM TFLOP/s & latency vs atomic; % rows bit-invariant across M/TP",
@@ -703,25 +1130,20 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_serial": round(ms_serial, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)/N(0,0.02)/N(1,0.1)/N(0,3) inputs of the 8B-like shapes)",
-        "config": {"workload": WORKLOAD, "global_batch": B, "parallelism": "none (1 GPU)"},
+        "config": {"workload": hd.workload, "global_batch": HEAD_M, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "ops": op_stats,
+        "headline_replays_identical": "%d/5" % same,
+        "step_b256": step,
         "det_vs_atomic": ratios,
         "replay_divergence": div,
         "extensions": ext,
         "configs": sweep,
-        "tree_tp_breakdown": tp,
-        "bit_invariant_rows_pct": round(100.0 * same / max(total, 1), 4),
-        "bit_invariant_rows_checked": total,
-        "det_replays_identical": "%d/20" % det_same,
-        "atomic_replays_differing": "%d/19" % atom_diff,
     }
     print(json.dumps(line), flush=True)
 
