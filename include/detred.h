@@ -50,6 +50,18 @@
  * the stream or on replay.  atomic_splitk_gemm is the only exception: it is
  * the nondeterministic control.
  *
+ * What is locked and what follows M.  P and Kc (the bits) depend on K only.
+ * The workgroup tile a call launches and the split that split_k = 0 picks
+ * are chosen for speed and DO depend on M (and on N and K): at most 64 rows
+ * run 64 x 128 tiles, 1024 rows or more of an eight-chunk product at one
+ * slice run 192 x 128 tiles, one-chunk shard roots with 256 rows or more
+ * (chunks of 1024 or more) run 256 x 256 tiles, outputs of at most 64
+ * columns run 64 x 16 tiles while 64 x 64 ones would leave fewer than 256
+ * workgroups, and detred_auto_split keys on M as described there.  None of
+ * these choices changes a bit: every tile evaluates the same chunk chains
+ * with the same MFMA k-slot layout and the same tree, and an output
+ * element's MFMA result does not depend on the row's place in the tile.
+ *
  * Requirements shared by the GEMM entry points (else the status shown):
  *   M, N, K >= 0; ldx >= K, ldw >= N, ldy >= N                   (EINVAL)
  *   X, W, Y 16-byte aligned; ldx, ldw multiples of 8; ldy of 4    (EINVAL)
@@ -88,12 +100,13 @@ const char *detred_status_string(detred_status status);
 int detred_version(void);
 
 /*
- * The locked policy for a product with N output columns and reduction
- * length K (it never depends on M).  Writes, where the pointer is non-NULL:
- *   chunks   = P (1 or 8) and chunk_k = Kc;
- *   tile_m, tile_n = the workgroup output tile for large M (an output of at
- *                    most 64 columns with few rows may run on 64 x 16 tiles;
- *                    no tile changes the bits);
+ * The locked reduction for reduction length K and the tile family for N
+ * output columns.  Writes, where the pointer is non-NULL:
+ *   chunks   = P (1 or 8) and chunk_k = Kc: these alone fix the bits;
+ *   tile_m, tile_n = the family's workgroup output tile (128 x 128 for wide
+ *                    outputs, 64 x 64 or 64 x 16 for narrow ones); the tile
+ *                    a call launches also follows M (see "What is locked
+ *                    and what follows M" above), never changing the bits;
  *   default_split  = the split split_k = 0 picks once M is large enough to
  *                    give every CU an output tile (detred_auto_split).
  * Returns EINVAL for N < 0 or K < 0.
@@ -129,9 +142,15 @@ size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards);
 
 /*
  * Zero a workspace's counters (the whole buffer) on stream s.  Call once
- * after allocating a workspace; every det_splitk_gemm call leaves the
- * counters at zero again when it completes.  One workspace serves one call
- * in flight at a time.
+ * after allocating a workspace.  The arrival counters are read only by the
+ * one-launch combine (split products of at most 64 columns with fewer than
+ * 16384 output elements); they must be zero when such a call starts, and
+ * every such call leaves them zero when it completes.  A workspace that was
+ * never zeroed, or that anything else has written since (another call's
+ * partials included, when the buffer is shared between shapes), gives
+ * those calls undefined results: the tree combine may run before every
+ * slice has arrived, or not at all.  The library does not detect this.
+ * One workspace serves one call in flight at a time.
  */
 detred_status detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
 

@@ -19,11 +19,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
 bool pow2_le8(int v) { return v == 1 || v == 2 || v == 4 || v == 8; }
 
+// ceil(a / b) for a >= 0, b > 0, without overflowing int on the way
+int cdiv(int a, int b) { return (int)(((long)a + b - 1) / b); }
+
 int chunk_count(int K) { return (K >= kChunkGranule && K % kChunkGranule == 0) ? kChunks : 1; }
 
-// The locked policy.  It is a function of (N, K) only, never of M, of the
-// split or of the shard count: the tile decides speed, the chunk tree
-// decides the bits.
+// The locked reduction (P, Kc: a function of K alone, they fix the bits)
+// and the tile family for N.  The tile a call launches and its split also
+// follow M (plan, narrow_for_decode, widen_for_rows, widen_for_roots,
+// auto_split): the tile decides speed, the chunk tree decides the bits.
 struct Policy {
     int P, Kc, tile, bm, bn, default_split;
 };
@@ -56,7 +60,7 @@ Policy plan(int M, int N, int K)
 {
     Policy p = policy_for(N, K);
     if (p.tile == TILE_M64 && N <= 64) {
-        const long wgs = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn) * p.default_split;
+        const long wgs = (long)cdiv(M, p.bm) * cdiv(N, p.bn) * p.default_split;
         if (wgs < 256) {
             p.tile = TILE_S16;
             tile_shape(p.tile, &p.bm, &p.bn);
@@ -71,7 +75,7 @@ size_t partial_bytes(int M, int N, int S) { return round_up((size_t)S * M * N * 
 
 size_t counter_bytes(const Policy& p, int M, int N)
 {
-    const size_t tm = (size_t)(M + p.bm - 1) / p.bm, tn = (size_t)(N + p.bn - 1) / p.bn;
+    const size_t tm = (size_t)cdiv(M, p.bm), tn = (size_t)cdiv(N, p.bn);
     return round_up(tm * tn * sizeof(unsigned), 256);
 }
 
@@ -118,8 +122,8 @@ GemmArgs make_args(const Policy& p, const uint16_t* X, int ldx, const uint16_t* 
     g.K = K;
     g.Kc = p.Kc;
     g.slices = slices;
-    g.tiles_m = (M + p.bm - 1) / p.bm;
-    g.tiles_n = (N + p.bn - 1) / p.bn;
+    g.tiles_m = cdiv(M, p.bm);
+    g.tiles_n = cdiv(N, p.bn);
     g.epi = 0;
     g.C = nullptr;
     g.ldc = 0;
@@ -142,8 +146,8 @@ void widen_for_roots(Policy& p, GemmArgs& g, int cps)
     if (p.tile != TILE_L128 || cps != 1 || p.Kc < 1024 || g.M < 256)
         return;
     GemmArgs w = g;
-    w.tiles_m = (g.M + 255) / 256;
-    w.tiles_n = (g.N + 255) / 256;
+    w.tiles_m = cdiv(g.M, 256);
+    w.tiles_n = cdiv(g.N, 256);
     if ((long)w.tiles_m * w.tiles_n * w.slices < 256 || !lds_engine_supports(TILE_L256, w, 1))
         return;
     // Roots that fit the 256 MiB MALL go out straight from the registers:
@@ -203,8 +207,8 @@ void widen_for_rows(Policy& p, GemmArgs& g, int cps)
     GemmArgs w = g;
     int bm = 0, bn = 0;
     tile_shape(TILE_W256, &bm, &bn);
-    w.tiles_m = (g.M + bm - 1) / bm;
-    w.tiles_n = (g.N + bn - 1) / bn;
+    w.tiles_m = cdiv(g.M, bm);
+    w.tiles_n = cdiv(g.N, bn);
     if (!lds_engine_supports(TILE_W256, w, cps))
         return;
     p.tile = TILE_W256;
@@ -235,7 +239,7 @@ int auto_split(const Policy& p, int M, int N)
 {
     if (p.tile != TILE_L128)
         return p.default_split;
-    const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+    const long tiles = (long)cdiv(M, p.bm) * cdiv(N, p.bn);
     const bool long_chunks = p.Kc >= 1024;
     int S = 1;
     if (p.Kc >= 1536 && M >= 256 && tiles >= 96) {
