@@ -144,7 +144,7 @@ size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards);
  * Zero a workspace's counters (the whole buffer) on stream s.  Call once
  * after allocating a workspace.  The arrival counters are read only by the
  * one-launch combine (split products of at most 64 columns with fewer than
- * 16384 output elements); they must be zero when such a call starts, and
+ * 65536 output elements); they must be zero when such a call starts, and
  * every such call leaves them zero when it completes.  A workspace that was
  * never zeroed, or that anything else has written since (another call's
  * partials included, when the buffer is shared between shapes), gives
@@ -162,7 +162,7 @@ detred_status detred_workspace_init(void *ws, size_t ws_bytes, detred_stream s);
  * subtree root into the workspace as S row-major [M][N] arrays (ld N) at
  * byte offset 0, and the top log2(S) levels of the tree add them into Y:
  * in a second launch that streams over the S arrays when N > 64 or
- * M*N >= 16384, otherwise (small narrow outputs) by the last slice of each
+ * M*N >= 65536, otherwise (small narrow outputs) by the last slice of each
  * output tile to finish, in the same launch.  Either way the bits are the
  * same.  ws may be NULL when S == 1.
  * ws must be 256-byte aligned and at least detred_gemm_workspace_bytes()

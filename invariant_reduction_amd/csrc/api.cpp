@@ -365,12 +365,13 @@ detred_status run_roots_then_combine(Policy p, GemmArgs g, int S, float* ws, hip
 // engine's roots go out with plain stores at full rate, where the last
 // arriver of each tile would read S partial tiles at the end of its own
 // work) and for outputs of at least kTwoPhaseMinElems elements; the
-// one-launch last-arriver combine only for small narrow outputs, where the
-// second launch would cost more than it saves.  Measured on MI355X, same
-// bits either way: 4096x4096x4096 at 8 slices 662 -> 385 us, 512x8192x8192
-// at 8 158 -> 108 us, 64x4096x4096 at 8 16.9 -> 14.5 us, 256x64x4096 at 8
-// 9.8 -> 9.1 us; 16x16x512 at 8 6.8 us in one launch against 8.0 in two.
-constexpr size_t kTwoPhaseMinElems = 16384;
+// one-launch last-arriver combine for narrow outputs below that, where a
+// second launch costs more than it saves.  Measured on MI355X, same bits
+// either way: 4096x4096x4096 at 8 slices 662 -> 385 us and 512x8192x8192 at
+// 8 158 -> 108 us in two launches; kernel time (rocprofv3) of the LoRA
+// shrink 256x64x4096 at 8 slices 7.96 us in two launches against 7.59 in
+// one (the atomic control: 7.4), at 4 slices 10.3 against 8.7 (atomic 9.7).
+constexpr size_t kTwoPhaseMinElems = 65536;
 
 // counters: where the arrival counters of a last-arriver combine live when
 // not in ws after the partials (the no-allocation entry point keeps them at

@@ -91,7 +91,7 @@ using TileD64 = LdsTile<64, 128, 2, 4>;
 // saved subtree level, which fit because the top level waits in the
 // workgroup's own output tile of Y between chunk 3 and chunk 7 (the call
 // needs no workspace).  Measured on MI355X against the 128x128 tile: 1024
-// rows of 4096x14336 205 -> 196 us, 4096 rows 635 -> 621 us.
+// rows of 4096x14336 205 -> 195 us, 4096 rows 635 -> 621 us.
 using TileW = LdsTile<192, 128, 2, 4>;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -975,7 +975,9 @@ __global__ __launch_bounds__(T::THREADS) void wide_gemm_kernel(GemmArgs g)
 template <bool WT>
 hipError_t launch_wide(const GemmArgs& g, hipStream_t s)
 {
-    constexpr int ST = 3;
+    // four stages fill the 160 KiB of LDS (3 -> 4 on MI355X: 4096x14336x4096
+    // 637 -> 621 us, 1024 rows 201 -> 195 us; three weight blocks in flight)
+    constexpr int ST = 4;
     auto fn = wide_gemm_kernel<TileW, ST, WT>;
     constexpr int bytes = ST * TileW::STAGE_BYTES;
     static_assert(bytes <= 160 * 1024, "LDS of one workgroup");

@@ -27,7 +27,7 @@ def noalloc(Xd, Wd, S, dev):
     return Y
 
 
-# (M, N, K, S): narrow outputs below 16384 elements combine in the last
+# (M, N, K, S): narrow outputs below 65536 elements combine in the last
 # arriving slice (counters); the others in a second launch over the roots
 SEQUENCE = [
     (200, 64, 4096, 8),     # last arriver, 4 x 4 tiles of counters
