@@ -157,6 +157,24 @@ __device__ __forceinline__ void dma16s(uint32_t lds_base, uint32_t voff, uint32_
 #pragma clang diagnostic pop
 }
 
+// dma16s through a buffer resource value (as made by
+// __builtin_amdgcn_make_buffer_rsrc), non-temporal: for data read once,
+// which should not push reused operand blocks out of the L2.
+__device__ __forceinline__ void dma16r(uint32_t lds_base, uint32_t voff, uint32_t soff,
+                                       __amdgpu_buffer_rsrc_t rs)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(rs), "s"(soff)
+        : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
 __device__ __forceinline__ void wait_lgkmcnt0()
 {
@@ -437,7 +455,9 @@ __device__ __forceinline__ void park_out_store(const ParkOut<T>& po, const f32x4
     constexpr int OOB = (int)0x80000000u;
     // the lane index made opaque, so that the store offsets are computed
     // here rather than hoisted out of the K loops (where they would hold
-    // registers for the whole kernel)
+    // registers for the whole kernel).  Full-tile slots take plain stores:
+    // their read-back is non-temporal (4096x14336x4096: 569 -> 560 us
+    // against non-temporal stores).
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
 #pragma unroll
@@ -449,7 +469,7 @@ __device__ __forceinline__ void park_out_store(const ParkOut<T>& po, const f32x4
                 const int off = ((sl / (T::BN / 4)) * po.ld + 4 * (sl % (T::BN / 4))) * 4;
                 const u32x4 q = {__float_as_uint(v[fm][fn][0]), __float_as_uint(v[fm][fn][1]),
                                  __float_as_uint(v[fm][fn][2]), __float_as_uint(v[fm][fn][3])};
-                __builtin_amdgcn_raw_buffer_store_b128(q, po.rs, off, 0, CPOL_NT);
+                __builtin_amdgcn_raw_buffer_store_b128(q, po.rs, off, 0, 0);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -773,11 +793,11 @@ __global__ __launch_bounds__(T::THREADS) void wide_gemm_kernel(GemmArgs g)
     }
     const uint32_t lda_bytes = (uint32_t)g.ldx * 2, ldw_bytes = (uint32_t)g.ldw * 2;
 
-    const int nb = (g.Kc + BK - 1) / BK;
+    // one slice, chunks of a whole number of K blocks: block t starts at k = 64 t
+    const int nb = g.Kc / BK;
     const int total = CPS * nb;
-    auto block_k = [&](int t) { return (t / nb) * g.Kc + (t % nb) * BK; };
     auto issue = [&](int t) {
-        const uint32_t kb = (uint32_t)block_k(t);
+        const uint32_t kb = (uint32_t)(t * BK);
         const uint32_t st = smem_lds + (uint32_t)((t % STAGES) * STAGE_BYTES);
 #pragma unroll
         for (int i = 0; i < LOADS_A; ++i)
@@ -916,8 +936,43 @@ __global__ __launch_bounds__(T::THREADS) void wide_gemm_kernel(GemmArgs g)
                 dst[fm][fn] = acc[fm][fn];
     };
 
+    // Read-back of the parked level on a full tile: each wave's FM*FN
+    // 16-byte slots per lane (one per accumulator, slot i = fm*FN + fn) are
+    // loaded by LDS-DMA into the stage buffers that the last blocks free,
+    // while those blocks are still multiplied: the first PARK_A slots into
+    // stage 0 after block total-4, the next PARK_A into stage 1 after
+    // total-3, the rest into stage 2 after total-2 (total = 8 nb, so block
+    // total-4 sat in stage 0).  Each lane loads only the slots it stored
+    // itself, so its own vmcnt is the only wait; a wave's region in stage p
+    // is PARK_A (p < 2) or PARK_C slots wide.
+    constexpr int SLOTS = FM * FN;
+    constexpr int PARK_A = STAGE_BYTES / 1024 / T::WAVES, PARK_C = SLOTS - 2 * PARK_A;
+    static_assert(STAGE_BYTES % (1024 * T::WAVES) == 0 && PARK_C >= 0 && PARK_C <= PARK_A &&
+                      STAGES == 4,
+                  "park read-back layout of the 192x128 tile");
+    auto park_lds = [&](int i) -> uint32_t {
+        const int p = i < PARK_A ? 0 : (i < 2 * PARK_A ? 1 : 2);
+        const int k = i - PARK_A * p;
+        return (uint32_t)(p * STAGE_BYTES + (wave * (p < 2 ? PARK_A : PARK_C) + k) * 1024);
+    };
+    const uint32_t ldy_bytes = (uint32_t)g.ldy * 4;
+    auto park_part = [&](int first, int count) {
+        // slot i covers tile rows 2(SLOTS wave + i) and the next, 16 bytes a lane
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const uint32_t pv = (uint32_t)(ln >> 5) * ldy_bytes + (uint32_t)(ln & 31) * 16;
+        for (int k = 0; k < count; ++k) {
+            const int i = first + k;
+            dma16r(smem_lds + park_lds(i), pv, (uint32_t)((wave * SLOTS + i) * 2) * ldy_bytes, po.rs);
+        }
+    };
+    const bool pf = po.full;
+
     // chunk c into acc: its MFMA chain from +0 over the chunk's K blocks
-    // (every block holds two k steps: Kc % 64 == 0 on this tile)
+    // (every block holds two k steps: Kc % 64 == 0 on this tile).  The
+    // vmcnt waits before each barrier admit exactly the loads issued after
+    // block t+1: two blocks in the steady state, then the last block and
+    // the read-back parts already in flight.
     auto chunk = [&](int c) {
         zero(acc);
         for (int b = 0; b < nb; ++b) {
@@ -928,14 +983,31 @@ __global__ __launch_bounds__(T::THREADS) void wide_gemm_kernel(GemmArgs g)
             kstep(acc, af, b0, b1, st, 1);
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkmcnt0();
-            if (t + STAGES - 1 < total)
+            if (t + STAGES - 1 < total) {
                 wait_vmcnt<(STAGES - 2) * LOADS_PER_ISSUE>();
-            else
-                wait_vmcnt<0>();
+            } else if (t == total - 3) {
+                if (pf)
+                    wait_vmcnt<LOADS_PER_ISSUE + PARK_A>();
+                else
+                    wait_vmcnt<LOADS_PER_ISSUE>();
+            } else if (t == total - 2) {
+                if (pf)
+                    wait_vmcnt<2 * PARK_A>();
+                else
+                    wait_vmcnt<0>();
+            }
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (t + STAGES < total)
+            if (t + STAGES < total) {
                 issue(t + STAGES);
+            } else if (pf) {
+                if (t == total - 4)
+                    park_part(0, PARK_A);
+                else if (t == total - 3)
+                    park_part(PARK_A, PARK_A);
+                else if (t == total - 2)
+                    park_part(2 * PARK_A, PARK_C);
+            }
             __builtin_amdgcn_sched_barrier(0);
             // the next block's reads are harmless after the last block
             kstep(acc, af, b1, b0, st_next, 0);
@@ -966,7 +1038,20 @@ __global__ __launch_bounds__(T::THREADS) void wide_gemm_kernel(GemmArgs g)
     add_left(keep0);                 // c6 + c7
     add_left(keep1);                 // (c4 + c5) + (c6 + c7)
     __builtin_amdgcn_sched_barrier(0);
-    park_out_add<T>(po, acc, lane);  // the left half + the right half
+    // the left half + the right half
+    if (pf) {
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const f32x4 left =
+                    *reinterpret_cast<const f32x4*>(smem + park_lds(fm * FN + fn) + lane * 16);
+                acc[fm][fn] = left + acc[fm][fn];
+            }
+    } else {
+        park_out_add<T>(po, acc, lane);
+    }
 
     // the final product through the stage buffers (addmm epilogue on the way)
     store_tile_via_lds<T, STAGES>(acc, g, g.Y, (int)g.ldy, row0, col0, wm, wn, lane, tid, smem);

@@ -17,9 +17,10 @@ from invariant_reduction_amd import detred, inputs
 pytestmark = pytest.mark.gpu
 
 # full tiles (1536 = 8 x 192 rows, 1024 = 8 x 128 columns), ragged rows and
-# columns, chunks of 512, 1024 and 1792
+# columns, chunks of 64, 128, 512, 1024 and 1792 (one and two K blocks per
+# chunk: the read-back of the parked level starts right after it is stored)
 SHAPES = [(1536, 1024, 4096), (1024, 14336, 4096), (1100, 200, 4096), (2000, 1032, 8192),
-          (1030, 264, 14336)]
+          (1030, 264, 14336), (1536, 256, 512), (1100, 264, 1024)]
 
 
 def det(Xd, Wd, S, dev):
