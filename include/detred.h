@@ -53,8 +53,11 @@
  * What is locked and what follows M.  P and Kc (the bits) depend on K only.
  * The workgroup tile a call launches and the split that split_k = 0 picks
  * are chosen for speed and DO depend on M (and on N and K): at most 64 rows
- * run 64 x 128 tiles, 1024 rows or more of an eight-chunk product at one
- * slice run 192 x 128 tiles, one-chunk shard roots with 256 rows or more
+ * run 64 x 128 tiles, an eight-chunk product at one slice runs 192 x 128
+ * tiles where 1.25 times their rounds of workgroups over the 256 compute
+ * units do not exceed those of 128 x 128 tiles (e.g. from 513 rows of a
+ * 14336-column output, from 1025 rows of a 4096-column one), one-chunk
+ * shard roots with 256 rows or more
  * (chunks of 1024 or more) run 256 x 256 tiles, outputs of at most 64
  * columns run 64 x 16 tiles while 64 x 64 ones would leave fewer than 256
  * workgroups, and detred_auto_split keys on M as described there.  None of

@@ -177,13 +177,20 @@ void narrow_for_decode(Policy& p, GemmArgs& g, int cps)
     g = w;
 }
 
-// Eight-chunk products of 1024 rows or more on the 192x128 tile (MI355X:
-// 1024 rows of 4096x14336 205 -> 196 us, 4096 rows 635 -> 621 us), whose
-// top subtree level waits in the product's own output rows of Y
-// (so the output must be fp32 and hold nothing the call still reads: no
-// bf16 output, and a C that overlaps Y keeps the 128x128 tile).  The tile
-// never changes the bits.
-constexpr int kWideMinRows = 1024;
+// Unsplit eight-chunk products on the 192x128 tile, whose top subtree level
+// waits in the product's own output rows of Y (so the output must be fp32
+// and hold nothing the call still reads: no bf16 output, and a C that
+// overlaps Y keeps the 128x128 tile), where it takes fewer rounds of
+// workgroups: each CU holds one workgroup of either tile, and a 192x128 tile
+// takes about 1.25 times as long as a 128x128 one (1.5 times the outputs at
+// a sixth less time per output), so it is taken when 1.25 x its rounds over
+// the 256 CUs do not exceed the 128x128 tile's.  On MI355X this picks the
+// faster tile on all 40 shapes of a sweep of M in 512..4096, N in
+// {4096, 8192, 14336}, K in {4096, 8192, 14336} (768x8192x8192 167 -> 111
+// us, 1280x4096x14336 283 -> 158 us, 4096x14336x4096 618 -> 539 us; the
+// 128x128 tile kept at 1024x4096x4096 47 vs 55 us, 512x8192x8192 99 vs 104
+// us).  The tile never changes the bits.
+constexpr long kComputeUnits = 256;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 {
@@ -193,7 +200,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 
 void widen_for_rows(Policy& p, GemmArgs& g, int cps)
 {
-    if (p.tile != TILE_L128 || cps != 8 || g.M < kWideMinRows || g.out_z_stride != 0)
+    if (p.tile != TILE_L128 || cps != 8 || g.out_z_stride != 0)
         return;
     if (g.epi && g.out_bf16)
         return;
@@ -209,7 +216,9 @@ void widen_for_rows(Policy& p, GemmArgs& g, int cps)
     tile_shape(TILE_W256, &bm, &bn);
     w.tiles_m = cdiv(g.M, bm);
     w.tiles_n = cdiv(g.N, bn);
-    if (!lds_engine_supports(TILE_W256, w, cps))
+    const long rounds = ((long)g.tiles_m * g.tiles_n + kComputeUnits - 1) / kComputeUnits;
+    const long rounds_w = ((long)w.tiles_m * w.tiles_n + kComputeUnits - 1) / kComputeUnits;
+    if (5 * rounds_w > 4 * rounds || !lds_engine_supports(TILE_W256, w, cps))
         return;
     p.tile = TILE_W256;
     p.bm = bm;

@@ -275,11 +275,21 @@ static void check_planner()
     CHECK(l.tile == TILE_D64 && l.cps == 8 && l.g.tiles_m == 1);
     l = plan1(65, 4096, 4096);
     CHECK(l.tile == TILE_L128 && l.g.tiles_m == 1);
-    // 1024 rows and more of an eight-chunk product: the 192x128 tile
-    l = plan1(1023, 14336, 4096);
-    CHECK(l.tile == TILE_L128 && l.g.tiles_m == 8 && l.g.tiles_n == 112);
-    l = plan1(1024, 14336, 4096);
-    CHECK(l.tile == TILE_W256 && l.g.tiles_m == 6 && l.g.tiles_n == 112 && l.cps == 8);
+    // an unsplit eight-chunk product takes the 192x128 tile where 1.25 x its
+    // rounds of workgroups over 256 CUs do not exceed the 128x128 tile's:
+    // 512 rows of 14336 columns take 2 rounds either way, 513 take 3 on
+    // 128x128 and 2 on 192x128; 1024 rows of 4096 take 1 either way, 1025
+    // take 2 and 1
+    l = plan1(512, 14336, 4096);
+    CHECK(l.tile == TILE_L128 && l.g.tiles_m == 4 && l.g.tiles_n == 112);
+    l = plan1(513, 14336, 4096);
+    CHECK(l.tile == TILE_W256 && l.g.tiles_m == 3 && l.g.tiles_n == 112 && l.cps == 8);
+    l = plan1(1024, 4096, 4096);
+    CHECK(l.tile == TILE_L128 && l.g.tiles_m == 8 && l.g.tiles_n == 32);
+    l = plan1(1025, 4096, 4096);
+    CHECK(l.tile == TILE_W256 && l.g.tiles_m == 6 && l.g.tiles_n == 32);
+    l = plan1(1280, 14336, 4096);   // 5 rounds on 128x128, 4 on 192x128: 5 <= 5
+    CHECK(l.tile == TILE_W256 && l.g.tiles_m == 7);
     l = plan1(4096, 14336, 4096);
     CHECK(l.tile == TILE_W256 && l.g.tiles_m == 22);
     // ...but not for one-chunk K, nor for a bf16 addmm output, nor when C
@@ -287,16 +297,16 @@ static void check_planner()
     l = plan1(2048, 4096, 264);
     CHECK(l.tile != TILE_W256 && l.cps == 1);
     launches.clear();
-    CHECK(det_splitk_addmm(X, 4096, W, 4096, nullptr, 0, 1.f, 0.f, Y, 4096, DETRED_BF16, 2048,
+    CHECK(det_splitk_addmm(X, 4096, W, 4096, nullptr, 0, 1.f, 0.f, Y, 4096, DETRED_BF16, 1280,
                            4096, 4096, 1, nullptr, 0, nullptr) == DETRED_OK);
     CHECK(launches.size() == 1 && launches[0].tile == TILE_L128);
     launches.clear();
-    CHECK(det_splitk_addmm(X, 4096, W, 4096, Y, 4096, 1.f, 1.f, Y, 4096, DETRED_F32, 2048, 4096,
+    CHECK(det_splitk_addmm(X, 4096, W, 4096, Y, 4096, 1.f, 1.f, Y, 4096, DETRED_F32, 1280, 4096,
                            4096, 1, nullptr, 0, nullptr) == DETRED_OK);
     CHECK(launches.size() == 1 && launches[0].tile == TILE_L128);
     launches.clear();
-    CHECK(det_splitk_addmm(X, 4096, W, 4096, Y + 2048 * 4096, 4096, 1.f, 1.f, Y, 4096, DETRED_F32,
-                           2048, 4096, 4096, 1, nullptr, 0, nullptr) == DETRED_OK);
+    CHECK(det_splitk_addmm(X, 4096, W, 4096, Y + 1280 * 4096, 4096, 1.f, 1.f, Y, 4096, DETRED_F32,
+                           1280, 4096, 4096, 1, nullptr, 0, nullptr) == DETRED_OK);
     CHECK(launches.size() == 1 && launches[0].tile == TILE_W256);
     // narrow outputs: 64x16 while 64x64 would leave fewer than 256
     // workgroups, else 64x64

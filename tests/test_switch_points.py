@@ -3,7 +3,9 @@ automatic split changes with M.  On each side of a switch the shared rows
 must be bit-identical (the chunk tree fixes the bits; the tile and the split
 only decide speed):
   * 64 / 65 rows:    64x128 tile -> 128x128 tile;
-  * 1023 / 1024 rows (eight chunks, one slice): 128x128 -> 192x128;
+  * 512 / 513 rows of a 14336-column output and 1024 / 1025 rows of a
+    4096-column one (eight chunks, one slice): 128x128 -> 192x128, where
+    the 192x128 tile starts to take fewer rounds of workgroups;
   * 255 / 256 rows, shard roots with chunks of 1024: 128x128 -> 256x256,
     roots compared directly;
   * 255 / 256 rows at K = 14336 (chunks of 1792): the automatic split
@@ -32,7 +34,8 @@ def det(Xd, Wd, S, dev):
 @pytest.mark.parametrize("N,K,S,Ms", [
     (4096, 4096, 1, (64, 65)),           # 64x128 -> 128x128
     (4096, 4096, 0, (64, 65)),
-    (2048, 4096, 1, (1023, 1024)),       # 128x128 -> 192x128
+    (14336, 4096, 1, (512, 513)),        # 128x128 -> 192x128
+    (4096, 4096, 1, (1024, 1025)),       # 128x128 -> 192x128
     (8192, 14336, 0, (255, 256)),        # automatic split -> 8 on 256x256
     (64, 4096, 8, (1984, 1985)),         # 64x16 -> 64x64
     (64, 4096, 8, (1023, 1024)),         # one-launch -> two-launch combine

@@ -1,12 +1,14 @@
-"""The 192x128 eight-chunk tile for products of 1024 rows or more (one
-slice): eight waves of 96x32, two saved subtree levels in registers and the
-top one parked in the product's own output rows between chunk 3 and 7.
+"""The 192x128 eight-chunk tile for unsplit products where it takes fewer
+rounds of workgroups than the 128x128 tile (1.25 x its rounds over 256 CUs
+at most the 128x128 tile's): eight waves of 96x32, two saved subtree levels
+in registers and the top one parked in the product's own output rows
+between chunk 3 and 7, read back by LDS-DMA into the freed stage buffers.
 
 Its bits must equal those of every other tile and split (here: 2 slices,
-which run the 128x128 engine and the combine launch, and batch prefixes
-below 1024 rows, which run the unsplit 128x128 tile), its values the
-oracle's; the park must not disturb anything outside the output's M x N
-elements, and an addmm whose C overlaps Y must still read C intact."""
+which run the 128x128 engine and the combine launch, and a batch prefix
+short enough for the unsplit 128x128 tile), its values the oracle's; the
+park must not disturb anything outside the output's M x N elements, and an
+addmm whose C overlaps Y must still read C intact."""
 import numpy as np
 import pytest
 import torch
@@ -16,11 +18,14 @@ from invariant_reduction_amd import detred, inputs
 
 pytestmark = pytest.mark.gpu
 
-# full tiles (1536 = 8 x 192 rows, 1024 = 8 x 128 columns), ragged rows and
-# columns, chunks of 64, 128, 512, 1024 and 1792 (one and two K blocks per
-# chunk: the read-back of the parked level starts right after it is stored)
-SHAPES = [(1536, 1024, 4096), (1024, 14336, 4096), (1100, 200, 4096), (2000, 1032, 8192),
-          (1030, 264, 14336), (1536, 256, 512), (1100, 264, 1024)]
+# (M, N, K, prefix): full tiles (1536 = 8 x 192 rows, 4096 = 32 x 128
+# columns), ragged rows and columns, chunks of 64, 128, 512, 1024 and 1792
+# (one and two K blocks per chunk: the read-back of the parked level starts
+# right after it is stored); the prefix rows alone take the 128x128 tile
+# (one round of workgroups either way)
+SHAPES = [(1536, 4096, 4096, 1024), (1024, 14336, 4096, 512), (1100, 4104, 4096, 896),
+          (2000, 4104, 8192, 896), (1030, 4200, 14336, 896), (1536, 4096, 512, 1024),
+          (1100, 4104, 1024, 896)]
 
 
 def det(Xd, Wd, S, dev):
@@ -31,8 +36,8 @@ def det(Xd, Wd, S, dev):
     return Y
 
 
-@pytest.mark.parametrize("M,N,K", SHAPES)
-def test_wide_tile_bits_and_parity(M, N, K, dev):
+@pytest.mark.parametrize("M,N,K,prefix", SHAPES)
+def test_wide_tile_bits_and_parity(M, N, K, prefix, dev):
     print("case wide %dx%dx%d" % (M, N, K), flush=True)
     X, W = inputs.dense_inputs(M, K, N, seed=5)
     Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
@@ -43,10 +48,10 @@ def test_wide_tile_bits_and_parity(M, N, K, dev):
     # rows across the tile edges and the ragged last tile row
     rows = sorted({0, 1, 191, 192, 383, M // 2, (M // 192) * 192 - 1, (M // 192) * 192, M - 1})
     assert_gemm_parity(y1, X, W, rows=[r for r in rows if r < M])
-    # the first 1000 rows alone run the unsplit 128x128 tile
-    yp = det(Xd[:1000], Wd, 1, dev)
+    # the prefix rows alone run the unsplit 128x128 tile
+    yp = det(Xd[:prefix], Wd, 1, dev)
     torch.cuda.synchronize()
-    assert_bitwise(yp, y1[:1000], "rows of 1000 alone vs the same rows in %d" % M)
+    assert_bitwise(yp, y1[:prefix], "rows of %d alone vs the same rows in %d" % (prefix, M))
 
 
 def test_wide_tile_integer_inputs_exact(dev):
@@ -70,7 +75,7 @@ def test_wide_tile_keeps_padding_and_addmm(dev):
     padding columns alone.  addmm with a bias row and with a separate C
     matrix equals its split-2 form bit for bit; with C overlapping Y (in
     place) the product still reads C intact."""
-    M, N, K = 1100, 1024, 4096
+    M, N, K = 1100, 4104, 4096
     X, W = inputs.dense_inputs(M, K, N, seed=6)
     Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
     buf = torch.full((M, N + 64), 123.0, dtype=torch.float32, device=dev)
@@ -104,7 +109,7 @@ def test_wide_tile_keeps_padding_and_addmm(dev):
 def test_wide_tile_transposed_weight_and_tree_tp(dev):
     """The transposed-weight layout on the 192x128 tile and tree-TP with one
     shard (which takes it) give the bits of eight shards."""
-    M, N, K = 1024, 4096, 8192
+    M, N, K = 1280, 4096, 8192
     X, W = inputs.dense_inputs(M, K, N, seed=8)
     Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
     y = det(Xd, Wd, 1, dev)
