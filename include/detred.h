@@ -123,12 +123,18 @@ detred_status detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m
  * result never depend on it (nor on M).  Outputs of at most 64 columns use
  * one slice per chunk (S = P).  For wider ones, with t = the number of
  * 128 x 128 output tiles and Kc = K / P:
- *   Kc >= 1536, M >= 256 and t >= 96: S = 8;
+ *   257 <= t <= 447, P = 8, Kc % 64 == 0 and ceil(M/192) * ceil(N/128) <=
+ *                   256 (one round of 192 x 128 tiles on the 256 compute
+ *                   units): S = 1;
+ *   else Kc >= 1536, M >= 256 and t >= 96: S = 8;
  *   else t <= 128:  the largest S (<= P) with t*S <= 256, but 4 instead of
  *                   2 for products of at most 16 rows;
  *   129 <= t < 192: S = 4 if Kc >= 1024, else 1;
  *   t >= 192:       S = 1, but for 257 <= t <= 447 S = 4 if Kc >= 1024,
  *                   else 2.
+ * This is the split of det_splitk_gemm and of an fp32 det_splitk_addmm
+ * whose C does not overlap Y.  An addmm into bf16, or with C overlapping Y,
+ * cannot run the 192 x 128 tile and skips the first rule.
  * Returns 0 for invalid arguments.
  */
 int detred_auto_split(int M, int N, int K);
@@ -137,7 +143,9 @@ int detred_auto_split(int M, int N, int K);
  * Workspace size in bytes that det_splitk_gemm (split_k = S) or tree_tp_gemm
  * (tp_shards = S) needs for an M x N output with reduction length K:
  * S fp32 partial arrays of M*N elements plus one 32-bit counter per output
- * tile, rounded up to 256 bytes.  S = 0 means detred_auto_split(M, N, K).
+ * tile, rounded up to 256 bytes.  S = 0 means the split a call with
+ * split_k = 0 picks: detred_auto_split(M, N, K), or, where larger, the split
+ * of an addmm that cannot run the 192 x 128 tile (see there).
  * 0 when S == 1 (no workspace is used), and 0 for a split the products reject
  * (S not in {1,2,4,8}, or S > P) and for invalid arguments.
  */

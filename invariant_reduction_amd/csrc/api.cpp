@@ -232,6 +232,9 @@ void widen_for_rows(Policy& p, GemmArgs& g, int cps)
 // the LDS engine's stage depth (four stages for a grid of at most 256
 // workgroups) and the cost of its slice roots, which a second launch
 // combines (t = output tiles of 128 x 128, Kc = chunk width):
+//  - 257 <= t <= 447 and the unsplit product fits one round of 192 x 128
+//    tiles (eight chunks of whole 64-wide K blocks, ceil(M/192) x
+//    ceil(N/128) <= 256, and a call that may take that tile: wide): unsplit;
 //  - Kc >= 1536 with at least 256 rows and t >= 96: 8 slices (one chunk
 //    each, on the 256x256 root tile: the long chunks amortise its
 //    prologue and epilogue);
@@ -243,18 +246,30 @@ void widen_for_rows(Policy& p, GemmArgs& g, int cps)
 // Measured on MI355X with the weights coming from HBM over M in 1..2560,
 // N in 1024..14336, K in {4096, 8192, 14336}, S in {1, 2, 4, 8}; e.g.
 // 128x14336x4096 45.2 -> 38.2 us (2 slices, not 4), 768x1024x4096 33.5 ->
-// 29.2 us (4, not 8), 384x8192x14336 at 8 slices 27 % faster than unsplit.
-int auto_split(const Policy& p, int M, int N)
+// 29.2 us (4, not 8), 384x8192x14336 at 8 slices 27 % faster than unsplit;
+// the first rule (unsplit on one round of 192x128 tiles) against the split
+// the others give there: 384x14336x4096 85 -> 66 us, 768x8192x8192 140 ->
+// 105 us, 1280x4096x4096 86 -> 62 us, 6144x1024x4096 87 -> 64 us,
+// 384x14336x14336 216 -> 194 us (640x8192x14336 175 vs 177 us).
+bool fits_one_wide_round(const Policy& p, int M, int N)
+{
+    return p.P == 8 && p.Kc % 64 == 0 && (long)cdiv(M, 192) * cdiv(N, 128) <= kComputeUnits;
+}
+
+int auto_split(const Policy& p, int M, int N, bool wide = true)
 {
     if (p.tile != TILE_L128)
         return p.default_split;
     const long tiles = (long)cdiv(M, p.bm) * cdiv(N, p.bn);
     const bool long_chunks = p.Kc >= 1024;
+    const bool band = tiles > 256 && tiles < 448;
     int S = 1;
-    if (p.Kc >= 1536 && M >= 256 && tiles >= 96) {
+    if (band && wide && fits_one_wide_round(p, M, N)) {
+        S = 1;
+    } else if (p.Kc >= 1536 && M >= 256 && tiles >= 96) {
         S = 8;
     } else if (tiles >= 192) {
-        if (tiles > 256 && tiles < 448)
+        if (band)
             S = long_chunks ? 4 : 2;
     } else if (tiles > 128) {
         S = long_chunks ? 4 : 1;
@@ -268,10 +283,11 @@ int auto_split(const Policy& p, int M, int N)
 }
 
 // Resolve split_k / tp_shards against the policy; 0 means auto_split.
-detred_status resolve_split(const Policy& p, int split, int M, int N, int* out)
+detred_status resolve_split(const Policy& p, int split, int M, int N, int* out,
+                            bool wide = true)
 {
     if (split == 0)
-        split = auto_split(p, M, N);
+        split = auto_split(p, M, N, wide);
     if (!pow2_le8(split) || split > p.P)
         return DETRED_EUNSUPPORTED;
     *out = split;
@@ -322,8 +338,14 @@ size_t detred_gemm_workspace_bytes(int M, int N, int K, int split_or_shards)
     if (M < 0 || N < 0 || K < 0)
         return 0;
     const Policy p = plan(M, N, K);
-    if (split_or_shards == 0)
-        split_or_shards = auto_split(p, M, N);
+    // split 0: enough for the split any call picks, also an addmm that
+    // cannot take the 192x128 tile (a bf16 output, or C overlapping Y)
+    if (split_or_shards == 0) {
+        const int a = auto_split(p, M, N, true), b = auto_split(p, M, N, false);
+        const size_t na = detred_gemm_workspace_bytes(M, N, K, a);
+        const size_t nb = detred_gemm_workspace_bytes(M, N, K, b);
+        return na > nb ? na : nb;
+    }
     // no workspace for one slice, none for a split the calls reject
     if (!pow2_le8(split_or_shards) || split_or_shards == 1 || split_or_shards > p.P)
         return 0;
@@ -489,7 +511,15 @@ detred_status det_addmm_impl(const uint16_t* X, int ldx, const uint16_t* W, int 
         return st;
     const Policy p = plan(M, N, K);
     int S = 0;
-    if ((st = resolve_split(p, split_k, M, N, &S)) != DETRED_OK)
+    // the 192x128 tile (and so the automatic split that counts on it) needs
+    // an fp32 output that holds nothing the call still reads
+    bool wide = y_dtype != DETRED_BF16;
+    if (wide && C) {
+        const size_t ybytes = ((size_t)(M - 1) * ldy + N) * sizeof(float);
+        const size_t cbytes = (ldc == 0 ? (size_t)N : (size_t)(M - 1) * ldc + N) * sizeof(float);
+        wide = !overlaps(Y, ybytes, C, cbytes);
+    }
+    if ((st = resolve_split(p, split_k, M, N, &S, wide)) != DETRED_OK)
         return st;
     GemmArgs g = make_args(p, X, ldx, W, ldw, (float*)Y, ldy, M, N, K, S);
     g.wt = wt;

@@ -315,6 +315,25 @@ static void check_planner()
     const size_t nws = detred_gemm_workspace_bytes(256, 64, 4096, 8);
     CHECK(det(256, 64, 4096, 8, ws_buf, nws) == DETRED_OK);
     CHECK(!launches.empty() && launches[0].tile == TILE_S16);
+    // the automatic split keeps one slice where the 128x128 grid would take
+    // 1.0-1.75 rounds and one round of 192x128 tiles holds the product
+    // (384 x 14336: 336 tiles of 128x128, 224 of 192x128); an addmm into
+    // bf16 cannot take that tile and keeps 2 slices, which the workspace of
+    // split 0 covers
+    {
+        void* big = (void*)(uintptr_t)0x40000000;
+        const size_t nbig = detred_gemm_workspace_bytes(384, 14336, 4096, 0);
+        CHECK(nbig == detred_gemm_workspace_bytes(384, 14336, 4096, 2));
+        CHECK(detred_auto_split(384, 14336, 4096) == 1);
+        launches.clear();
+        CHECK(det(384, 14336, 4096, 0, big, nbig) == DETRED_OK);
+        CHECK(launches.size() == 1 && launches[0].tile == TILE_W256 && launches[0].cps == 8);
+        launches.clear();
+        CHECK(det_splitk_addmm(X, 4096, W, 14336, nullptr, 0, 1.f, 0.f, Y, 14336, DETRED_BF16, 384,
+                               14336, 4096, 0, big, nbig, nullptr) == DETRED_OK);
+        CHECK(!launches.empty() && launches[0].tile == TILE_L128 && launches[0].cps == 4 &&
+              launches[0].g.slices == 2);
+    }
     // the automatic split: 8 slices for chunks of 1792 with 256+ rows (on
     // the 256x256 root tile), none at 4096 x 14336 x 4096
     CHECK(detred_auto_split(256, 8192, 14336) == 8);

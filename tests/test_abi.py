@@ -69,8 +69,12 @@ def test_auto_split():
     assert detred.auto_split(1, 1024, 4096) == 8         # 8 tiles, capped at P
     assert detred.auto_split(640, 4096, 4096) == 1       # 160 tiles, chunks of 512
     assert detred.auto_split(640, 4096, 8192) == 4       # 160 tiles, chunks of 1024
-    assert detred.auto_split(384, 14336, 8192) == 4      # 336 tiles, chunks of 1024
-    assert detred.auto_split(384, 14336, 4096) == 2      # 336 tiles, chunks of 512
+    assert detred.auto_split(384, 14336, 8192) == 1      # 336 tiles, one round of 192x128
+    assert detred.auto_split(384, 14336, 4096) == 1      # 336 tiles, one round of 192x128
+    assert detred.auto_split(1280, 4096, 4096) == 1      # 320 tiles, one round of 192x128
+    assert detred.auto_split(1664, 4096, 4096) == 2      # 416 tiles, 288 of 192x128
+    assert detred.auto_split(384, 14336, 14336) == 1     # 336 tiles, one round of 192x128
+    assert detred.auto_split(256, 14336, 14336) == 8     # 224 tiles, chunks of 1792
     assert detred.auto_split(384, 8192, 14336) == 8      # chunks of 1792, 256+ rows
     assert detred.auto_split(128, 14336, 14336) == 2     # chunks of 1792, 128 rows
     assert detred.auto_split(512, 14336, 8192) == 1      # 448 tiles
@@ -81,6 +85,10 @@ def test_auto_split():
     assert detred.detred_gemm_workspace_bytes(256, 4096, 4096, 0) == \
         detred.detred_gemm_workspace_bytes(256, 4096, 4096, 4)
     assert detred.detred_gemm_workspace_bytes(256, 14336, 4096, 0) == 0
+    # split 0 also covers an addmm that cannot take the 192x128 tile (bf16
+    # output), which keeps the 2 slices of 336 tiles with chunks of 512
+    assert detred.detred_gemm_workspace_bytes(384, 14336, 4096, 0) == \
+        detred.detred_gemm_workspace_bytes(384, 14336, 4096, 2) > 0
 
 
 def test_workspace_bytes():
@@ -314,15 +322,19 @@ def test_torch_mode_registers_and_restores():
     assert not torch_ops.is_enabled()
 
 
-def _documented_split(M, N, K):
+def _documented_split(M, N, K, wide=True):
     """The automatic split as include/detred.h states it, written out here
-    independently of the library."""
+    independently of the library (wide: the call may take the 192 x 128
+    tile, as det_splitk_gemm always may)."""
     P = 8 if (K >= 256 and K % 256 == 0) else 1
     if N <= 64 or P == 1:
         return None  # narrow outputs and one-chunk K keep the policy's split
     Kc = K // P
     t = ((M + 127) // 128) * ((N + 127) // 128)
-    if Kc >= 1536 and M >= 256 and t >= 96:
+    one_wide_round = Kc % 64 == 0 and ((M + 191) // 192) * ((N + 127) // 128) <= 256
+    if wide and 257 <= t <= 447 and one_wide_round:
+        S = 1
+    elif Kc >= 1536 and M >= 256 and t >= 96:
         S = 8
     elif t <= 128:
         S = 1
@@ -358,6 +370,9 @@ def test_workspace_sizes_cover_the_partial_planes():
                 for S in (0, 1, 2, 4, 8):
                     got = L.detred_gemm_workspace_bytes(M, N, K, S)
                     s = S if S else detred.auto_split(M, N, K)
+                    if S == 0:
+                        # also the split of a call that cannot take the 192x128 tile
+                        s = max(s, _documented_split(M, N, K, wide=False) or 0)
                     P = 8 if (K >= 256 and K % 256 == 0) else 1
                     if s <= 1 or s > P:
                         if s <= 1:
