@@ -129,8 +129,8 @@ detred_status detred_policy(int N, int K, int *chunks, int *chunk_k, int *tile_m
  *   else Kc >= 1536, M >= 256 and t >= 96: S = 8;
  *   else t <= 128:  the largest S (<= P) with t*S <= 256, but 4 instead of
  *                   2 for products of at most 16 rows;
- *   129 <= t < 192: S = 4 if Kc >= 1024, else 1;
- *   t >= 192:       S = 1, but for 257 <= t <= 447 S = 4 if Kc >= 1024,
+ *   129 <= t <= 192: S = 4 if Kc >= 1024, else 1;
+ *   t > 192:        S = 1, but for 257 <= t <= 447 S = 4 if Kc >= 1024,
  *                   else 2.
  * This is the split of det_splitk_gemm and of an fp32 det_splitk_addmm
  * whose C does not overlap Y.  An addmm into bf16, or with C overlapping Y,

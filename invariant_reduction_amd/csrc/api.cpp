@@ -240,8 +240,10 @@ void widen_for_rows(Policy& p, GemmArgs& g, int cps)
 //    prologue and epilogue);
 //  - t <= 128: the most slices that keep the grid at or under 256
 //    workgroups, except 4 rather than 2 for products of at most 16 rows;
-//  - 129 <= t < 192: 4 slices for Kc >= 1024, else unsplit;
-//  - t >= 192: unsplit, except for 257..447 tiles (1.0-1.75 waves of
+//  - 129 <= t <= 192: 4 slices for Kc >= 1024, else unsplit (at t = 192
+//    with chunks of 1024, cold: 320x8192x8192 97 -> 82 us, 700x4096x8192
+//    86 -> 82 us);
+//  - t > 192: unsplit, except for 257..447 tiles (1.0-1.75 waves of
 //    workgroups unsplit): 4 slices for Kc >= 1024, 2 for shorter chunks.
 // Measured on MI355X with the weights coming from HBM over M in 1..2560,
 // N in 1024..14336, K in {4096, 8192, 14336}, S in {1, 2, 4, 8}; e.g.
@@ -268,7 +270,7 @@ int auto_split(const Policy& p, int M, int N, bool wide = true)
         S = 1;
     } else if (p.Kc >= 1536 && M >= 256 && tiles >= 96) {
         S = 8;
-    } else if (tiles >= 192) {
+    } else if (tiles > 192) {
         if (band)
             S = long_chunks ? 4 : 2;
     } else if (tiles > 128) {

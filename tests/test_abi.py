@@ -57,8 +57,9 @@ def test_policy_is_locked_by_n_and_k():
 
 def test_auto_split():
     # wide outputs: the most slices that keep the grid at <= 256 workgroups
-    # below 129 tiles, unsplit from 192 tiles, 4 slices between with long
-    # chunks and for 257..447 tiles with long chunks
+    # below 129 tiles, unsplit above 192 tiles, 4 slices between with long
+    # chunks and for 257..447 tiles with long chunks (unless one round of
+    # 192x128 tiles holds the product)
     assert detred.auto_split(256, 14336, 4096) == 1      # 224 tiles
     assert detred.auto_split(1, 14336, 4096) == 4        # 112 tiles, at most 16 rows
     assert detred.auto_split(32, 14336, 4096) == 2       # 112 tiles
@@ -69,6 +70,8 @@ def test_auto_split():
     assert detred.auto_split(1, 1024, 4096) == 8         # 8 tiles, capped at P
     assert detred.auto_split(640, 4096, 4096) == 1       # 160 tiles, chunks of 512
     assert detred.auto_split(640, 4096, 8192) == 4       # 160 tiles, chunks of 1024
+    assert detred.auto_split(320, 8192, 8192) == 4       # 192 tiles, chunks of 1024
+    assert detred.auto_split(768, 4096, 4096) == 1       # 192 tiles, chunks of 512
     assert detred.auto_split(384, 14336, 8192) == 1      # 336 tiles, one round of 192x128
     assert detred.auto_split(384, 14336, 4096) == 1      # 336 tiles, one round of 192x128
     assert detred.auto_split(1280, 4096, 4096) == 1      # 320 tiles, one round of 192x128
@@ -342,7 +345,7 @@ def _documented_split(M, N, K, wide=True):
             S *= 2
         if S == 2 and M <= 16:
             S = 4
-    elif t < 192:
+    elif t <= 192:
         S = 4 if Kc >= 1024 else 1
     else:
         S = (4 if Kc >= 1024 else 2) if 257 <= t <= 447 else 1

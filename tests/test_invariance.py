@@ -69,14 +69,14 @@ def test_dense_rows_invariant_across_m(dev):
 
 
 @pytest.mark.parametrize("N,K,Ms", [(4096, 4096, (200, 256, 512, 700)),
-                                     (1024, 8192, (1024, 2048, 3000))])
+                                     (1024, 8192, (1024, 2048, 3100))])
 def test_rows_invariant_across_lds_stage_depth(N, K, Ms, dev):
-    """The 128x128 engine keeps four LDS stages for grids of at most 256
-    workgroups and two above; the automatic split also changes with M.  The
-    shared rows must not notice: here 200, 256 and 1024 rows run 4 slices on
-    256 workgroups (four stages), 512 and 2048 rows 4 slices on 512 (two),
-    and the reference rows run unsplit (three stages beside the parked tree
-    level)."""
+    """The 128x128 engine's LDS stage depth follows its grid and the
+    automatic split changes with M.  The shared rows must not notice: here
+    200, 256 and 1024 rows take 4 slices and 512 and 2048 rows 2 slices (256
+    workgroups, four stages each), while the reference rows (700 and 3100)
+    run unsplit with eight chunks per workgroup (three stages beside the
+    parked tree level)."""
     M = Ms[-1]
     X, W = inputs.dense_inputs(M, K, N, seed=11)
     Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
