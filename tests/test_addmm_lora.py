@@ -121,6 +121,26 @@ def test_addmm_bf16_output_is_rounded_fp32_output(M, N, K, dev):
         np.testing.assert_array_equal(u16(Yb), oracle.f32_to_bf16(host(Yf)))
 
 
+@pytest.mark.parametrize("M,N,K", [(384, 14336, 4096), (1280, 4096, 4096)])
+def test_addmm_automatic_split_bf16_and_fp32(M, N, K, dev):
+    """At these shapes the automatic split keeps one slice for an fp32
+    output (one round of 192x128 tiles) but splits an addmm into bf16,
+    which cannot take that tile; one workspace sized for split 0 serves both
+    calls, and the bf16 output is the fp32 output rounded to nearest even."""
+    assert detred.auto_split(M, N, K) == 1
+    X, W = inputs.dense_inputs(M, K, N, seed=13)
+    Xd, Wd = dev_bf16(X, dev), dev_bf16(W, dev)
+    bias = dev_f32(inputs.bias_inputs(N, seed=4), dev)
+    ws = detred.workspace(M, N, K, 0, dev)
+    assert ws is not None and ws.numel() == detred.detred_gemm_workspace_bytes(M, N, K, 2)
+    Yf = torch.empty((M, N), dtype=torch.float32, device=dev)
+    Yb = torch.empty((M, N), dtype=torch.int16, device=dev)
+    detred.det_splitk_addmm(Xd, Wd, Yf, bias, 0.75, 1.0, 0, ws)
+    detred.det_splitk_addmm(Xd, Wd, Yb, bias, 0.75, 1.0, 0, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u16(Yb), oracle.f32_to_bf16(host(Yf)))
+
+
 def test_addmm_integer_inputs_exact(dev):
     # integer inputs and C, dyadic coefficients: every value exact in fp32
     M, N, K = 129, 264, 2048
