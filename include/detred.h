@@ -57,10 +57,10 @@
  * tiles where 1.25 times their rounds of workgroups over the 256 compute
  * units do not exceed those of 128 x 128 tiles (e.g. from 513 rows of a
  * 14336-column output, from 1025 rows of a 4096-column one), one-chunk
- * shard roots with 256 rows or more
- * (chunks of 1024 or more) run 256 x 256 tiles, outputs of at most 64
- * columns run 64 x 16 tiles while 64 x 64 ones would leave fewer than 256
- * workgroups, and detred_auto_split keys on M as described there.  None of
+ * shard roots with 256 rows or more (chunks of 1024 or more) run 256 x 256
+ * tiles, outputs of at most 64 columns run 64 x 16 tiles while 64 x 64 ones
+ * would leave fewer than 256 workgroups, and detred_auto_split keys on M as
+ * described there.  None of
  * these choices changes a bit: every tile evaluates the same chunk chains
  * with the same MFMA k-slot layout and the same tree, and an output
  * element's MFMA result does not depend on the row's place in the tile.
